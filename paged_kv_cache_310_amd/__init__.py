@@ -1,0 +1,18 @@
+"""MI355X-native paged KV cache: decode attention through block tables,
+paged KV append and copy-on-write block copy, as hand-written HIP kernels for
+gfx950 behind a C ABI (``include/pa.h``), with a thin ctypes binding.
+
+The binding (``pa_append_kv``, ``pa_copy_blocks``, ``pa_decode``,
+``pa_decode_workspace_size``) is loaded lazily from ``_binding`` so that the
+host-only modules (block manager, workload generator) import without a GPU.
+"""
+
+__all__ = ["pa_append_kv", "pa_copy_blocks", "pa_decode", "pa_decode_workspace_size",
+           "pa_status_string", "library_path", "PAError"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)
