@@ -1,0 +1,140 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged KV-cache library (libpa.so).
+ *
+ * Three device operations on a pool of fixed-size KV blocks:
+ *   pa_append_kv    write new tokens' keys/values into the slots a slot mapping names;
+ *   pa_copy_blocks  copy whole blocks (the copy in copy-on-write);
+ *   pa_decode       one decode step of attention for every sequence, reading each
+ *                   sequence's keys/values through its block table.
+ *
+ * Sources: the pages on "Efficient Memory Management for Large Language Model
+ * Serving with PagedAttention" -- zeroshotmind.com essay, sections "Paging the
+ * cache" (fixed-size blocks, 16 tokens by default, allocated on demand),
+ * "Block tables: logical order, physical scatter" (per-sequence table, logical
+ * block index -> physical block number; attention walks the logical order),
+ * "Sharing a prefix without copying it" (ref-counted shared blocks; a write
+ * into a shared block duplicates that one block); phantomic12.github.io
+ * catalogue note, method paragraph (attention kernels read through the block
+ * table).  The attention itself is scaled dot-product attention
+ * softmax(q . K^T * scale) . V over all cached tokens of the sequence.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer to caller-owned, contiguous,
+ *    row-major memory, 16-byte aligned.  The library allocates nothing,
+ *    frees nothing and keeps no pointer after returning.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns; results are visible in stream order.
+ *  - `dtype` (pa_dtype) is the element type of q, out, both pools and the
+ *    new K/V; there is no conversion anywhere, so data movement is bit-exact.
+ *  - Pools: k_cache, v_cache are [num_blocks, num_kv_heads, block_size, head_dim].
+ *    Slot s of the pool is physical block s / block_size, offset s % block_size.
+ *  - Supported: head_dim in {64, 128}; block_size in {16, 32}; dtype fp32 or
+ *    bf16; num_q_heads a multiple of num_kv_heads.
+ *  - Return value: PA_OK (0) or a pa_status error.  Scalar arguments are
+ *    checked before any HIP call.  Index data lives on the device and is NOT
+ *    checked by default (that would need a device->host copy): out-of-range
+ *    blocks or slots, duplicate slots, or copy pairs that alias are undefined
+ *    behaviour.  With the environment variable PA_CHECK=1 every call copies
+ *    its index arrays to the host, synchronising `stream`, and returns
+ *    PA_ERR_INDEX instead of launching when they break the contract.
+ *  - The library never prints, throws or aborts.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,     /* bad scalar argument or NULL pointer              */
+  PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, block_size, dtype */
+  PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
+  PA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed       */
+  PA_ERR_INDEX = 5        /* PA_CHECK=1 found index data breaking the contract */
+} pa_status;
+
+typedef enum pa_dtype { PA_DTYPE_FP32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+
+/* Paged KV append.  Page: "Paging the cache" (a new token goes into the
+ * sequence's tail block, a fresh block only when the tail is full; the host
+ * block manager picks the slot).
+ *   k_new, v_new   [num_tokens, num_kv_heads, head_dim]      read
+ *   slot_mapping   int64 [num_tokens]; slot < 0 = skip token  read
+ *   k_cache[slot / block_size, :, slot % block_size, :] = k_new[t]  (same for V)
+ * Every other byte of the pools is left unchanged.  Contract: slots in
+ * [0, num_blocks*block_size) or negative; no slot repeats.  num_tokens == 0
+ * is a no-op. */
+int pa_append_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                 const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                 int num_kv_heads, int block_size, int head_dim, int dtype, void* stream);
+
+/* Copy-on-write block copy.  Page: "Sharing a prefix without copying it"
+ * (duplicate just the one shared block being written).
+ *   block_mapping  int64 [num_pairs][2] = (src, dst)           read
+ *   k_cache[dst] = k_cache[src]; v_cache[dst] = v_cache[src]  (all heads, all slots)
+ * Contract: ids in [0, num_blocks); no dst repeats; no dst equals any src of the
+ * same call (so the result never depends on copy order).  num_pairs == 0 is a
+ * no-op. */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
+                   int64_t num_blocks, int num_kv_heads, int block_size, int head_dim,
+                   int dtype, void* stream);
+
+/* Bytes of device workspace pa_decode needs for these sizes and `num_workers`
+ * (0 = the library's default for the current device).  Writes *bytes.  The
+ * workspace holds per-worker partial results and per-(sequence, head)
+ * completion counters.  It must be zero-filled before its first use; every
+ * pa_decode call leaves the counters zero again, so one workspace can be
+ * reused by successive calls in stream order (never by two calls at once). */
+int pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                             int num_workers, size_t* bytes);
+
+/* Number of workers (64-lane wavefronts, one per workgroup) pa_decode uses by
+ * default on the current device.  Writes *num_workers. */
+int pa_decode_default_workers(int* num_workers);
+
+/* Decode-step paged attention.  Pages: "Block tables: logical order, physical
+ * scatter" (walk logical blocks in order through the table, gather K/V) and
+ * the catalogue note's method paragraph (attention reads through the table).
+ *   out            [num_seqs, num_q_heads, head_dim]                 written
+ *   q              [num_seqs, num_q_heads, head_dim]                 read
+ *   block_tables   int32 [num_seqs, max_blocks_per_seq]              read
+ *   context_lens   int32 [num_seqs]: tokens cached for the sequence
+ *                  AFTER this step's append (0 = empty -> out row is 0)
+ *   For query head h, KV head kvh = h / (num_q_heads / num_kv_heads):
+ *     out[s,h] = sum_j softmax_j(scale * q[s,h] . K_j) V_j over positions
+ *     j < context_lens[s], position j stored in block
+ *     block_tables[s][j / block_size] at offset j % block_size.
+ *   Fused append: k_new, v_new ([num_seqs, num_kv_heads, head_dim]) and
+ *     slot_mapping (int64 [num_seqs]) are all NULL, or all set.  When set,
+ *     token s is sequence s's newest token: the call behaves exactly like
+ *     pa_append_kv(k_new, v_new, slot_mapping, num_seqs) followed by
+ *     pa_decode without them.  Contract: slot_mapping[s] is negative or the
+ *     slot of position context_lens[s]-1 of sequence s.
+ *   workspace      see pa_decode_workspace_size (read/written)
+ *   num_workers    0 = default; otherwise the exact number of workers, a
+ *                  tuning knob that changes only the fp32 summation order.
+ * Contract: 0 <= context_lens[s] <= max_blocks_per_seq * block_size; table
+ * entries for the blocks a sequence uses lie in [0, num_blocks); entries past
+ * them are never read. */
+int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq,
+              const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+              int head_dim, int block_size, int64_t num_blocks, float scale,
+              const void* k_new, const void* v_new, const int64_t* slot_mapping,
+              void* workspace, size_t workspace_bytes, int num_workers,
+              int dtype, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

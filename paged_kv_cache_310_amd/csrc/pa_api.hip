@@ -1,0 +1,265 @@
+// Host side of the C ABI declared in include/pa.h: argument checks, optional
+// index validation (PA_CHECK=1), workspace sizing and kernel dispatch.
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+bool check_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("PA_CHECK");
+    return v != nullptr && v[0] != '\0' && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool shape_ok(int dtype, int num_kv_heads, int block_size, int head_dim, int64_t num_blocks) {
+  (void)dtype;
+  return num_kv_heads > 0 && block_size > 0 && head_dim > 0 && num_blocks > 0;
+}
+
+int support_status(int dtype, int block_size, int head_dim) {
+  if (dtype != PA_DTYPE_FP32 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+template <typename I>
+bool copy_to_host(std::vector<I>& dst, const I* src, size_t n, hipStream_t stream) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(I), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return false;
+  return hipStreamSynchronize(stream) == hipSuccess;
+}
+
+// Compute units of the current device (cached per device).
+int current_device_cus(int* out) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return PA_ERR_HIP;
+    cache[dev] = cus;
+  }
+  *out = cache[dev];
+  return PA_OK;
+}
+
+// Upper bound of the default worker count: CUs x kWavesPerCu.
+int default_workers_for_current_device(int* out) {
+  int cus = 0;
+  const int st = current_device_cus(&cus);
+  if (st != PA_OK) return st;
+  *out = cus * pa::kWavesPerCu;
+  return PA_OK;
+}
+
+// Default workers of one kernel variant: every worker resident at once.
+int default_workers_for_variant(int dtype, int head_dim, int block_size, int* out) {
+  int cus = 0;
+  const int st = current_device_cus(&cus);
+  if (st != PA_OK) return st;
+  int resident = 0;
+  if (pa::decode_resident_per_cu(dtype, head_dim, block_size, &resident) != hipSuccess ||
+      resident <= 0)
+    return PA_ERR_HIP;
+  *out = cus * (resident < pa::kWavesPerCu ? resident : pa::kWavesPerCu);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or dtype";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_INDEX: return "index data breaks the contract (PA_CHECK)";
+    default: return "unknown status";
+  }
+}
+
+int pa_append_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                 const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                 int num_kv_heads, int block_size, int head_dim, int dtype, void* stream) {
+  if (num_tokens < 0 || !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks))
+    return PA_ERR_INVALID;
+  const int sup = support_status(dtype, block_size, head_dim);
+  if (sup != PA_OK) return sup;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return PA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    std::vector<int64_t> slots;
+    if (!copy_to_host(slots, slot_mapping, (size_t)num_tokens, st)) return PA_ERR_HIP;
+    std::vector<char> seen((size_t)(num_blocks * block_size), 0);
+    for (int64_t s : slots) {
+      if (s < 0) continue;
+      if (s >= num_blocks * block_size || seen[(size_t)s]) return PA_ERR_INDEX;
+      seen[(size_t)s] = 1;
+    }
+  }
+  const int row_bytes = head_dim * pa::elem_bytes(dtype);
+  return pa::launch_append(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens, num_kv_heads,
+                           block_size, row_bytes, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
+                   int64_t num_blocks, int num_kv_heads, int block_size, int head_dim,
+                   int dtype, void* stream) {
+  if (num_pairs < 0 || !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks))
+    return PA_ERR_INVALID;
+  const int sup = support_status(dtype, block_size, head_dim);
+  if (sup != PA_OK) return sup;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_INVALID;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    std::vector<int64_t> pairs;
+    if (!copy_to_host(pairs, block_mapping, (size_t)(2 * num_pairs), st)) return PA_ERR_HIP;
+    std::vector<char> role((size_t)num_blocks, 0);   // 1 = src, 2 = dst
+    for (int64_t p = 0; p < num_pairs; ++p) {
+      const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+      if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return PA_ERR_INDEX;
+      if (role[(size_t)dst] != 0) return PA_ERR_INDEX;   // dst repeats or is a src
+      if (role[(size_t)src] == 2) return PA_ERR_INDEX;   // src is an earlier dst
+      role[(size_t)src] = 1;
+      role[(size_t)dst] = 2;
+    }
+  }
+  const int64_t block_bytes =
+      (int64_t)num_kv_heads * block_size * head_dim * pa::elem_bytes(dtype);
+  return pa::launch_copy(k_cache, v_cache, block_mapping, num_pairs, block_bytes, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int pa_decode_default_workers(int* num_workers) {
+  if (!num_workers) return PA_ERR_INVALID;
+  return default_workers_for_current_device(num_workers);
+}
+
+int pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                             int num_workers, size_t* bytes) {
+  if (!bytes || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_workers < 0 || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_INVALID;
+  int workers = num_workers;
+  if (workers == 0) {
+    const int st = default_workers_for_current_device(&workers);
+    if (st != PA_OK) return st;
+  }
+  *bytes = pa::counters_bytes(num_seqs, num_q_heads) +
+           pa::partials_bytes(workers, num_q_heads / num_kv_heads, head_dim);
+  return PA_OK;
+}
+
+int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq,
+              const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+              int head_dim, int block_size, int64_t num_blocks, float scale,
+              const void* k_new, const void* v_new, const int64_t* slot_mapping,
+              void* workspace, size_t workspace_bytes, int num_workers,
+              int dtype, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_workers < 0 ||
+      !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks) ||
+      num_q_heads % num_kv_heads != 0 || !(scale == scale))
+    return PA_ERR_INVALID;
+  const int sup = support_status(dtype, block_size, head_dim);
+  if (sup != PA_OK) return sup;
+  const int fused = (k_new != nullptr) + (v_new != nullptr) + (slot_mapping != nullptr);
+  if (fused != 0 && fused != 3) return PA_ERR_INVALID;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (fused && (!aligned16(k_new) || !aligned16(v_new))))
+    return PA_ERR_INVALID;
+  if ((int64_t)num_seqs * num_q_heads > INT32_MAX) return PA_ERR_UNSUPPORTED;
+
+  int workers = num_workers;
+  if (workers == 0) {
+    const int st = default_workers_for_variant(dtype, head_dim, block_size, &workers);
+    if (st != PA_OK) return st;
+  }
+  const int group = num_q_heads / num_kv_heads;
+  const size_t need = pa::counters_bytes(num_seqs, num_q_heads) +
+                      pa::partials_bytes(workers, group, head_dim);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    std::vector<int32_t> lens, tables;
+    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, st)) return PA_ERR_HIP;
+    if (!copy_to_host(tables, block_tables, (size_t)num_seqs * max_blocks_per_seq, st))
+      return PA_ERR_HIP;
+    std::vector<int64_t> slots;
+    if (fused && !copy_to_host(slots, slot_mapping, (size_t)num_seqs, st)) return PA_ERR_HIP;
+    for (int s = 0; s < num_seqs; ++s) {
+      const int64_t L = lens[(size_t)s];
+      if (L < 0 || L > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_INDEX;
+      const int64_t nblk = (L + block_size - 1) / block_size;
+      for (int64_t j = 0; j < nblk; ++j) {
+        const int64_t b = tables[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= num_blocks) return PA_ERR_INDEX;
+      }
+      if (fused && slots[(size_t)s] >= 0) {
+        if (L < 1) return PA_ERR_INDEX;
+        const int64_t last = L - 1;
+        const int64_t want =
+            (int64_t)tables[(size_t)s * max_blocks_per_seq + last / block_size] * block_size +
+            last % block_size;
+        if (slots[(size_t)s] != want) return PA_ERR_INDEX;
+      }
+    }
+  }
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.counters = static_cast<int*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        pa::counters_bytes(num_seqs, num_q_heads));
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return pa::launch_decode(a, dtype, head_dim, block_size, workers, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+}  // extern "C"

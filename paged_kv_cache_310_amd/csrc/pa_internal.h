@@ -1,0 +1,65 @@
+// Internal declarations shared by the HIP translation units of libpa.so.
+// Not part of the public ABI (that is include/pa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// CDNA4 (gfx950) dispatches consecutive workgroup ids round-robin over its
+// 8 accelerator dies (XCDs), each with a private L2.
+constexpr int kNumXcd = 8;
+// Tokens handled per decode inner-loop step ("chunk"); block sizes are
+// multiples of it.
+constexpr int kChunk = 16;
+
+enum DType : int { kFp32 = 0, kBf16 = 1 };
+
+inline int elem_bytes(int dtype) { return dtype == kBf16 ? 2 : 4; }
+
+// Everything the decode kernels read, in one POD passed by value.
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const void* k_new;          // fused append, or nullptr
+  const void* v_new;
+  const int64_t* slot_mapping;
+  int* counters;              // [num_seqs * num_q_heads] completion counters
+  float* partials;            // [workers][2][group][head_dim + 2]
+  int64_t max_blocks_per_seq;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                  // num_q_heads / num_kv_heads
+  float scale_log2;           // scale * log2(e): scores live in the exp2 domain
+};
+
+// Workspace layout (bytes): counters first, then per-worker partials.
+inline size_t counters_bytes(int num_seqs, int num_q_heads) {
+  size_t b = (size_t)num_seqs * (size_t)num_q_heads * sizeof(int);
+  return (b + 255) & ~(size_t)255;
+}
+inline size_t partials_bytes(int workers, int group, int head_dim) {
+  return (size_t)workers * 2 * (size_t)group * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,
+                         int workers, hipStream_t stream);
+// Resident decode workers (one-wave workgroups) per CU for a variant.
+hipError_t decode_resident_per_cu(int dtype, int head_dim, int block_size, int* resident);
+hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                         int block_size, int row_bytes, hipStream_t stream);
+hipError_t launch_copy(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                       int64_t num_pairs, int64_t block_bytes, hipStream_t stream);
+
+// Upper bound on decode workers per CU used to size workspaces (4 waves per
+// SIMD); a variant's default is min(this, its resident waves per CU).
+constexpr int kWavesPerCu = 16;
+
+}  // namespace pa

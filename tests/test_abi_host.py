@@ -1,0 +1,108 @@
+"""The C ABI without a GPU: the library loads into the process torch's HIP
+runtime lives in, exports exactly what include/pa.h declares, and rejects bad
+scalar arguments before making any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (loads torch's HIP runtime before libpa.so)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_cache_310_amd import _binding, build
+    if not os.path.exists(_binding.library_path()):
+        build.build()
+    return _binding._load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+
+
+def test_exports_match_header(lib):
+    from paged_kv_cache_310_amd import _binding
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == declared_functions()
+    for name in exported:
+        assert hasattr(lib, name)
+
+
+def test_single_hip_runtime_in_process(lib):
+    maps = open("/proc/self/maps").read()
+    hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(hip) == 1, hip
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.pa_status_string(code)
+    assert lib.pa_status_string(99) == b"unknown status"
+
+
+def test_workspace_size_formula(lib):
+    sz = ctypes.c_size_t(0)
+    assert lib.pa_decode_workspace_size(32, 40, 40, 128, 4096, ctypes.byref(sz)) == 0
+    counters = (32 * 40 * 4 + 255) // 256 * 256
+    assert sz.value == counters + 4096 * 2 * 1 * 130 * 4
+    assert lib.pa_decode_workspace_size(256, 64, 8, 128, 100, ctypes.byref(sz)) == 0
+    assert sz.value == (256 * 64 * 4 + 255) // 256 * 256 + 100 * 2 * 8 * 130 * 4
+    assert lib.pa_decode_workspace_size(4, 6, 4, 64, 8, ctypes.byref(sz)) == 1   # 6 % 4 != 0
+
+
+FAKE = 1 << 20   # an aligned address that is never dereferenced: checks fail first
+
+
+def decode_status(lib, **kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tab=FAKE, mb=4, lens=FAKE, b=2, hq=8, hkv=8,
+                d=128, bs=16, nb=10, scale=0.1, kn=None, vn=None, sm=None, ws=None, wsb=0,
+                workers=64, dtype=1)
+    args.update(kw)
+    return lib.pa_decode(args["out"], args["q"], args["k"], args["v"], args["tab"], args["mb"],
+                         args["lens"], args["b"], args["hq"], args["hkv"], args["d"], args["bs"],
+                         args["nb"], args["scale"], args["kn"], args["vn"], args["sm"], args["ws"],
+                         args["wsb"], args["workers"], args["dtype"], None)
+
+
+def test_decode_rejects_bad_scalars_before_any_hip_call(lib):
+    assert decode_status(lib, d=96) == 2
+    assert decode_status(lib, bs=8) == 2
+    assert decode_status(lib, dtype=7) == 2
+    assert decode_status(lib, hq=6, hkv=4) == 1
+    assert decode_status(lib, b=-1) == 1
+    assert decode_status(lib, mb=0) == 1
+    assert decode_status(lib, scale=float("nan")) == 1
+    assert decode_status(lib, kn=FAKE) == 1               # fused arguments go together
+    assert decode_status(lib, q=None) == 1
+    assert decode_status(lib, q=FAKE + 4) == 1            # not 16-byte aligned
+    assert decode_status(lib) == 3                        # no workspace
+    assert decode_status(lib, ws=FAKE, wsb=16) == 3       # workspace too small
+    assert decode_status(lib, b=0) == 0                   # nothing to do
+
+
+def test_append_and_copy_reject_bad_scalars(lib):
+    assert lib.pa_append_kv(None, None, None, None, None, 0, 10, 8, 16, 128, 1, None) == 0
+    assert lib.pa_append_kv(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 8, 16, 96, 1, None) == 2
+    assert lib.pa_append_kv(None, FAKE, FAKE, FAKE, FAKE, 3, 10, 8, 16, 128, 1, None) == 1
+    assert lib.pa_append_kv(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 10, 8, 16, 128, 1, None) == 1
+    assert lib.pa_copy_blocks(None, None, None, 0, 10, 8, 16, 128, 1, None) == 0
+    assert lib.pa_copy_blocks(FAKE, FAKE, FAKE, 2, 10, 8, 32, 64, 3, None) == 2
+    assert lib.pa_copy_blocks(FAKE, FAKE, None, 2, 10, 8, 32, 64, 0, None) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from paged_kv_cache_310_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _binding._load()
