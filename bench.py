@@ -1,0 +1,254 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: the step's copy-on-write
+block copies (if the workload has any), the paged append of each sequence's
+newest token and decode attention over every cached token -- the append is
+fused into the decode launch when the workload appends.  Default workload:
+``llama13b_long`` (32 sequences, 40 MHA heads of 128, 16-token blocks,
+lognormal lengths with median 4096 clipped to [1024, 16384], bf16).
+
+Prints ONE JSON line: achieved HBM GB/s on the KV bytes the step reads
+(``value``), sequence-steps per second, the decode kernel's roofline entry
+(HIP-event timing of each launch on the stream it runs on) and the CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (KV read) & % of peak; seq-steps/sec"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, vendor specification
+DECODE_KERNEL = "decode_valu_kernel"
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_310_amd", "csrc", "decode_kernel.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llama13b_long")
+    p.add_argument("--workers", type=int, default=0, help="decode workers (0 = library default)")
+    p.add_argument("--cold-steps", type=int, default=20,
+                   help="extra steps, each after a 512 MiB write that evicts the MALL")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU oracle time budget for the baseline sample (0 = skip)")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    of this workload, or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source sha256\[:16\]: `([0-9a-f]+)`", text)
+    t = re.search(r"hbm bytes per launch \(calibrated\): `([0-9.e+]+)`", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle on whole sequences (all heads) of the workload,
+    in a fixed seeded order, until the time budget is used."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    k, v = w.k_cache, w.v_cache
+    if w.slot_mapping is not None:
+        k, v = oracle.append_kv(k, v, w.k_new, w.v_new, w.slot_mapping, w.block_size)
+    order = np.random.default_rng(0).permutation(w.num_seqs)
+    done_bytes, seqs = 0, 0
+    per_tok = 2 * w.num_kv_heads * w.head_dim * (2 if w.dtype == "bf16" else 4)
+    t0 = time.perf_counter()
+    for s in order:
+        rows = [(int(s), h) for h in range(w.num_q_heads)]
+        oracle.decode(w.q, k, v, w.block_tables, w.context_lens, w.scale, w.dtype, w.block_size,
+                      rows=rows)
+        done_bytes += int(w.context_lens[s]) * per_tok
+        seqs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{seqs} of {w.num_seqs} sequences (all {w.num_q_heads} heads, "
+                  f"{done_bytes / 1e9:.3f} GB of KV) in {dt:.1f} s, fp64 numpy, "
+                  f"seq-steps/s {seqs / dt:.3f}; cpu '{cpu}', "
+                  f"os.cpu_count {os.cpu_count()}, affinity {len(os.sched_getaffinity(0))}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this path runs without collectives or sharding; "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_310_amd as pa
+    from paged_kv_cache_310_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "launches": 3}))
+        return
+
+    t0 = time.perf_counter()
+    w = wl.make_workload(args.workload, poison=False)
+    log(f"workload {w.name}: {w.num_seqs} seqs, {int(w.context_lens.sum())} tokens, "
+        f"{w.kv_bytes / 1e9:.3f} GB KV, generated in {time.perf_counter() - t0:.1f} s")
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, k, v = to_dev(w.q), to_dev(w.k_cache), to_dev(w.v_cache)
+    tables, lens = to_dev(w.block_tables), to_dev(w.context_lens)
+    k_new, v_new, slots, pairs = to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping), \
+        to_dev(w.block_mapping)
+    out = torch.empty_like(q)
+    ws_bytes = pa.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                           args.workers)
+    workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if pairs is not None:
+            pa.pa_copy_blocks(k, v, pairs)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_decode(q, k, v, tables, lens, float(w.scale), out=out, k_new=k_new, v_new=v_new,
+                     slot_mapping=slots, workspace=workspace, num_workers=args.workers)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    kernel_ms = np.array([a.elapsed_time(b) for a, b in events])
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Steps after evicting the 256 MiB MALL (outside any timed region).
+    cold_ms = None
+    if args.cold_steps:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(args.cold_steps):
+            flush.fill_(1)
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            step(ev)
+            torch.cuda.synchronize()
+            cold.append(ev[0].elapsed_time(ev[1]))
+        cold_ms = float(np.median(cold))
+        del flush
+
+    kv = w.kv_bytes
+    avg_kernel_s = float(kernel_ms.mean()) / 1e3
+    achieved = kv / avg_kernel_s / 1e9
+    value = kv / (ms_per_step / 1e3) / 1e9
+    traffic = counter_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+            "context_tokens": int(w.context_lens.sum()), "kv_bytes_per_step": kv,
+            "step": ("copy + " if pairs is not None else "")
+                    + ("fused append + decode" if slots is not None else "decode"),
+            "workers": args.workers or "default",
+        },
+        "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "seq_steps_per_s": round(w.num_seqs / (ms_per_step / 1e3), 1),
+        "decode_kernel_ms": {"mean": round(float(kernel_ms.mean()), 5),
+                             "median": round(float(np.median(kernel_ms)), 5),
+                             "p10": round(float(np.percentile(kernel_ms, 10)), 5),
+                             "p90": round(float(np.percentile(kernel_ms, 90)), 5),
+                             "cold_median_after_mall_flush": None if cold_ms is None else round(cold_ms, 5)},
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": DECODE_KERNEL, "kernel_source_sha256_16": kernel_source_hash(),
+        },
+        "device": torch.cuda.get_device_name(dev),
+        "host": platform.node(),
+    }
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle baseline ...")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
