@@ -87,15 +87,16 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
 
 /* Bytes of device workspace pa_decode needs for these sizes and `num_workers`
  * (0 = the library's default for the current device).  Writes *bytes.  The
- * workspace holds per-worker partial results and per-(sequence, head)
- * completion counters.  It must be zero-filled before its first use; every
- * pa_decode call leaves the counters zero again, so one workspace can be
- * reused by successive calls in stream order (never by two calls at once). */
+ * workspace holds per-worker partial results of the context split:
+ * num_workers * 2 * (num_q_heads / num_kv_heads) * (head_dim + 2) floats.
+ * It needs no initialisation; one workspace serves successive calls of any
+ * shape in stream order (never two calls at once). */
 int pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              int num_workers, size_t* bytes);
 
-/* Number of workers (64-lane wavefronts, one per workgroup) pa_decode uses by
- * default on the current device.  Writes *num_workers. */
+/* Upper bound of the number of workers (64-lane wavefronts, one per
+ * workgroup) pa_decode uses by default on the current device -- the count
+ * pa_decode_workspace_size assumes for num_workers = 0.  Writes *num_workers. */
 int pa_decode_default_workers(int* num_workers);
 
 /* Decode-step paged attention.  Pages: "Block tables: logical order, physical

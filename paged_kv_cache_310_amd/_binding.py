@@ -150,8 +150,8 @@ _workspaces = {}
 
 
 def decode_workspace(device, nbytes: int) -> torch.Tensor:
-    """A zero-filled workspace of at least ``nbytes`` for ``device``, reused
-    by later calls in stream order (each call leaves its counters zero)."""
+    """A workspace of at least ``nbytes`` for ``device``, reused by later
+    calls on the same device in stream order."""
     device = torch.device(device)
     key = (device.type, device.index)
     ws = _workspaces.get(key)

@@ -99,7 +99,10 @@ class BlockManager:
         """Register a sequence already holding ``length`` tokens."""
         if seq in self.tables:
             raise KeyError(f"sequence {seq} exists")
-        self.tables[seq] = [self.allocate() for _ in range(blocks_needed(length, self.block_size))]
+        need = blocks_needed(length, self.block_size)
+        if need > len(self.free):          # all or nothing: no partial allocation
+            raise PoolExhausted(f"{need} blocks needed, {len(self.free)} free")
+        self.tables[seq] = [self.allocate() for _ in range(need)]
         self.lengths[seq] = int(length)
 
     def append_slot(self, seq: int) -> Tuple[int, Optional[Tuple[int, int]]]:

@@ -28,21 +28,33 @@
 //    are merged once per piece.
 //  * Loads for chunk j+1 are in flight while chunk j is computed.
 //  * A segment that spans two or more workers leaves (max, sum, acc) partials
-//    in the workspace; the last worker to finish it (device-scope counter)
-//    merges them in worker order and writes the output, then resets the
-//    counter.  Segments inside one worker are written directly.
+//    in the workspace and a second, small kernel merges them in worker order.
+//    Segments inside one worker are written directly.  (Merging inside the
+//    decode launch would need a device-scope release/acquire per partial,
+//    which on this multi-XCD part writes back and invalidates the XCD's L2
+//    each time; measured, that cost grew with the worker count and halved
+//    throughput.)
 //  * Workgroup ids are remapped so that consecutive workers run on the same
 //    XCD: sequences that share prefix blocks (consecutive in the chunk line)
 //    then meet in one L2.
-//  * Fused append: the worker that owns a segment's last chunk reads the
-//    newest token from k_new/v_new instead of the pool and writes it to its
-//    slot, which no other worker reads in the same launch.
+//  * Fused append: the worker that owns a segment's last chunk takes the
+//    newest token from k_new/v_new (its pool slot is masked in the loop),
+//    and writes it to its slot, which no other worker reads in this launch.
 #include "pa_internal.h"
+
+// No implicit a*b+c fusion in this file: a rounded score must be the same
+// value in the running maximum and in its exponent (so the maximum's weight
+// is exactly 1).  Every intended FMA is written as fmaf().
+#pragma clang fp contract(off)
 
 namespace pa {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Read-only index data (block tables) is read through the constant address
+// space so that wave-uniform reads become scalar loads: they are counted by
+// lgkmcnt, so waiting for a table entry never waits for in-flight tile loads.
+typedef const int32_t __attribute__((address_space(4))) const_i32;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource for one tile: scalar 48-bit base, byte range [0, bytes).
@@ -224,6 +236,48 @@ __device__ void locate_sequence(const int32_t* lens, int num_seqs, int64_t r, in
   before = acc;
 }
 
+// The chunk line: all (head, sequence, 16-token chunk) triples, head-major,
+// split into equal contiguous ranges [b0, b1) over the workers.
+struct LineSplit {
+  int64_t wseq;   // chunks per head: sum over sequences of ceil(L / 16)
+  int64_t W;      // chunks in the line
+  int64_t NW;     // workers with a non-empty range: min(workers, W)
+  int64_t b0, b1;
+};
+
+// Computes the split for worker w; false when w has no chunks.
+__device__ __forceinline__ bool split_line(const int32_t* lens, int num_seqs, int num_heads,
+                                           int nworkers, int w, int lane, LineSplit& ls) {
+  int64_t wseq = 0;
+  for (int base = 0; base < num_seqs; base += 256) {
+    int64_t n = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = base + k * 64 + lane;
+      if (s < num_seqs) n += chunks_of(lens[s]);
+    }
+    wseq += uniform(wave_sum(n));
+  }
+  ls.wseq = wseq;
+  ls.W = wseq * num_heads;
+  if (ls.W == 0) return false;
+  ls.NW = ls.W < nworkers ? ls.W : nworkers;
+  if (w >= ls.NW) return false;
+  ls.b0 = (int64_t)w * ls.W / ls.NW;
+  ls.b1 = (int64_t)(w + 1) * ls.W / ls.NW;
+  return true;
+}
+
+// The segment (head h, sequence s) holding chunk c, and where it starts.
+__device__ __forceinline__ void locate_segment(const int32_t* lens, int num_seqs, int64_t wseq,
+                                               int64_t c, int lane, int& h, int& s,
+                                               int64_t& seg_start) {
+  h = (int)(c / wseq);
+  int64_t before = 0;
+  locate_sequence(lens, num_seqs, c - (int64_t)h * wseq, lane, s, before);
+  seg_start = (int64_t)h * wseq + before;
+}
+
 template <typename T, int D>
 struct Tile {
   u32x4 k[Geo<T, D>::kNl];
@@ -262,31 +316,14 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     }
   }
 
-  // Length of the chunk line.
-  int64_t wseq = 0;
-  for (int base = 0; base < B; base += 256) {
-    int64_t n = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = base + k * 64 + lane;
-      if (s < B) n += chunks_of(lens[s]);
-    }
-    wseq += uniform(wave_sum(n));
-  }
-  const int64_t W = wseq * HQ;
-  if (W == 0) return;
-  const int64_t NW = W < nworkers ? W : nworkers;
-  if (w >= NW) return;
-  const int64_t b0 = (int64_t)w * W / NW;
-  const int64_t b1 = (int64_t)(w + 1) * W / NW;
-
-  int h = (int)(b0 / wseq);
-  int s = 0;
-  int64_t before = 0;
-  locate_sequence(lens, B, b0 - (int64_t)h * wseq, lane, s, before);
+  LineSplit ls;
+  if (!split_line(lens, B, HQ, nworkers, w, lane, ls)) return;
+  const int64_t b0 = ls.b0, b1 = ls.b1;
+  int h = 0, s = 0;
+  int64_t seg_start = 0;
+  locate_segment(lens, B, ls.wseq, b0, lane, h, s, seg_start);
   int L = lens[s];
   int n = chunks_of(L);
-  int64_t seg_start = (int64_t)h * wseq + before;
   int64_t c = b0;
 
   const int64_t block_stride = (int64_t)HKV * BS * ROW;
@@ -301,21 +338,29 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     const int kvh = h / a.group;
     const u32x4 qv = load16(tile_rsrc(static_cast<const char*>(a.q) + ((size_t)s * HQ + h) * ROW, ROW),
                             col * 16);
-    // Fused append: this worker owns position L-1 when it holds the last chunk.
+    // Fused append: the worker holding the segment's last chunk owns position
+    // L-1.  It masks that position in the pooled tiles, folds the token in from
+    // k_new/v_new after the chunk loop and stores it to its slot, so the loop
+    // itself has no conditional loads or stores.
     int64_t slot = -1;
     if (a.slot_mapping != nullptr && j1 == n) slot = a.slot_mapping[s];
     const bool app = slot >= 0;
-    const int app_tok = (L - 1) & (kChunk - 1);
-    const char* knew = static_cast<const char*>(a.k_new) + ((size_t)s * HKV + kvh) * ROW;
-    const char* vnew = static_cast<const char*>(a.v_new) + ((size_t)s * HKV + kvh) * ROW;
+    const int L_pool = app ? L - 1 : L;   // positions read from the pool
+    u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+    if (app) {
+      const char* knew = static_cast<const char*>(a.k_new) + ((size_t)s * HKV + kvh) * ROW;
+      const char* vnew = static_cast<const char*>(a.v_new) + ((size_t)s * HKV + kvh) * ROW;
+      kn = load16(tile_rsrc(knew, ROW), col * 16);
+      vn = load16(tile_rsrc(vnew, ROW), col * 16);
+    }
 
-    const int32_t* __restrict__ tab = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    const int nblk = (L + BS - 1) / BS;
+    const const_i32* tab =
+        (const const_i32*)(a.block_tables + (int64_t)s * a.max_blocks_per_seq);
     const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * BS * ROW;
     const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * BS * ROW;
 
-    int win_base = j0 / CPB;   // block-table window: entries win_base .. win_base+63
-    int win = (win_base + lane < nblk) ? tab[win_base + lane] : 0;
+    // Physical block of the next chunk to issue, read one chunk ahead.
+    int next_pb = tab[j0 / CPB];
 
     float m = -INFINITY, l = 0.f;
     float o[EPL];
@@ -323,12 +368,8 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     for (int e = 0; e < EPL; ++e) o[e] = 0.f;
 
     auto issue = [&](Tile<T, D>& t, int j) {
-      const int jb = j / CPB;
-      if (jb - win_base >= 64) {
-        win_base = jb;
-        win = (win_base + lane < nblk) ? tab[win_base + lane] : 0;
-      }
-      const int pb = __builtin_amdgcn_readlane(win, jb - win_base);
+      const int pb = next_pb;
+      next_pb = tab[(j + 1 < j1 ? j + 1 : j) / CPB];
       const int64_t off = (int64_t)pb * block_stride + (int64_t)(j % CPB) * kChunk * ROW;
       const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + off, kChunk * ROW);
       const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + off, kChunk * ROW);
@@ -337,18 +378,8 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
         t.k[i] = load16(kr, i * 1024 + lane * 16);
         t.v[i] = load16(vr, i * 1024 + lane * 16);
       }
-      if (app && j == n - 1) {
-        // The newest token comes from k_new/v_new, not from its (stale) slot.
-        const __amdgpu_buffer_rsrc_t knr = tile_rsrc(knew, ROW);
-        const __amdgpu_buffer_rsrc_t vnr = tile_rsrc(vnew, ROW);
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          if (i * TPL + trow == app_tok) {
-            t.k[i] = load16(knr, col * 16);
-            t.v[i] = load16(vnr, col * 16);
-          }
-        }
-      }
+      // Keep the loads ahead of the math on the other tile.
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     auto consume = [&](const Tile<T, D>& t, int j) {
@@ -357,7 +388,7 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
       for (int i = 0; i < NL; ++i) {
         const float dot = row_sum<LPT>(dot16<T>(qv, t.k[i]));
         const int tok = j * kChunk + i * TPL + trow;
-        sc[i] = tok < L ? dot * a.scale_log2 : -INFINITY;
+        sc[i] = tok < L_pool ? dot * a.scale_log2 : -INFINITY;
       }
       float mx = sc[0];
 #pragma unroll
@@ -372,35 +403,56 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
       for (int i = 0; i < NL; ++i) {
         const float p = fast_exp2(sc[i] - m_use);
         l += p;
-        const bool ok = j * kChunk + i * TPL + trow < L;
+        const bool ok = j * kChunk + i * TPL + trow < L_pool;
         const u32x4 vv = ok ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
         axpy16<T>(o, p, vv);
       }
       m = m_new;
-      if (app && j == n - 1 && h % a.group == 0) {
-        const int64_t blk = slot / BS;
-        const int64_t pos = slot - blk * BS;
-        const int64_t row_off = ((blk * HKV + kvh) * BS + pos) * ROW + col * 16;
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          if (i * TPL + trow == app_tok) {
-            *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) + row_off) = t.k[i];
-            *reinterpret_cast<u32x4*>(static_cast<char*>(a.v_cache) + row_off) = t.v[i];
-          }
-        }
-      }
     };
 
     // Two tiles in ping-pong: the loads of one are in flight while the other
     // is consumed (no register copies, so no wait on the in-flight loads).
+    // The steady-state loop issues unconditionally, so every path into a
+    // consume has the same loads in flight and the compiler waits only for
+    // the tile being consumed; the last one or two chunks are peeled.
     Tile<T, D> ta, tb;
     issue(ta, j0);
-    for (int j = j0; j < j1; j += 2) {
-      if (j + 1 < j1) issue(tb, j + 1);
+    int j = j0;
+    for (; j + 2 < j1; j += 2) {
+      issue(tb, j + 1);
       consume(ta, j);
-      if (j + 1 >= j1) break;
-      if (j + 2 < j1) issue(ta, j + 2);
+      issue(ta, j + 2);
       consume(tb, j + 1);
+    }
+    if (j + 1 < j1) {
+      issue(tb, j + 1);
+      consume(ta, j);
+      consume(tb, j + 1);
+    } else {
+      consume(ta, j);
+    }
+
+    if (app) {
+      // The newest token joins token row 0; its K/V row goes to its slot.
+      const float dot = row_sum<LPT>(dot16<T>(qv, kn));
+      if (trow == 0) {
+        const float sc = dot * a.scale_log2;
+        const float m_new = fmaxf(m, sc);
+        const float alpha = fast_exp2(m - m_new);
+        const float p = fast_exp2(sc - m_new);
+        l = l * alpha + p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] *= alpha;
+        axpy16<T>(o, p, vn);
+        m = m_new;
+        if (h % a.group == 0) {
+          const int64_t blk = slot / BS;
+          const int64_t pos = slot - blk * BS;
+          const int64_t row_off = ((blk * HKV + kvh) * BS + pos) * ROW + col * 16;
+          *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) + row_off) = kn;
+          *reinterpret_cast<u32x4*>(static_cast<char*>(a.v_cache) + row_off) = vn;
+        }
+      }
     }
 
     // Merge the token rows of the wavefront (lanes with equal col).
@@ -425,7 +477,8 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     if (j0 == 0 && j1 == n) {
       if (lane < LPT) store_out16<T>(out_row + col * 16, o, 1.f / l);
     } else {
-      // Partial piece: publish (max, sum, acc) and let the last arrival merge.
+      // Partial piece: publish (max, sum, acc); the merge kernel, which runs
+      // after this launch, combines the pieces of the segment.
       const int which = seg_start <= b0 ? 0 : 1;
       float* P = a.partials + ((int64_t)w * 2 + which) * a.group * (D + 2);
       if (lane < LPT) {
@@ -435,35 +488,6 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
       if (lane == 0) {
         P[D] = m;
         P[D + 1] = l;
-      }
-      __threadfence();
-      const int seg_id = h * B + s;
-      int prev = 0;
-      if (lane == 0) prev = atomicAdd(a.counters + seg_id, 1);
-      prev = uniform(__shfl(prev, 0));
-      const int64_t wa = worker_of(seg_start, W, NW);
-      const int64_t wb = worker_of(seg_end - 1, W, NW);
-      if (prev == wb - wa) {
-        __threadfence();
-        float M = -INFINITY, S = 0.f;
-        float O[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) O[e] = 0.f;
-        for (int64_t ww = wa; ww <= wb; ++ww) {
-          const int64_t bw = ww * W / NW;
-          const float* Pp = a.partials + (ww * 2 + (seg_start <= bw ? 0 : 1)) * a.group * (D + 2);
-          const float mp = Pp[D];
-          const float lp = Pp[D + 1];
-          const float mn = fmaxf(M, mp);
-          const float fa = fast_exp2(M - mn);
-          const float fb = fast_exp2(mp - mn);
-          S = S * fa + lp * fb;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) O[e] = O[e] * fa + Pp[col * EPL + e] * fb;
-          M = mn;
-        }
-        if (lane < LPT) store_out16<T>(out_row + col * 16, O, 1.f / S);
-        if (lane == 0) a.counters[seg_id] = 0;
       }
     }
     // ------------------------------------------------------------ next piece
@@ -481,6 +505,48 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
   }
 }
 
+// Merges the partial pieces of every segment that spans several workers.
+// Worker w's wave acts for the segment holding chunk b0 of its range when
+// that segment started in an earlier worker and ends inside this range: it
+// folds the pieces of workers wa..w in worker order (deterministic) and
+// writes the output row.  Runs after the decode launch in stream order, so
+// the partials are visible without any in-kernel fence.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void merge_kernel(const DecodeArgs a) {
+  using G = Geo<T, D>;
+  constexpr int LPT = G::kLpt, EPL = G::kEpl, ROW = G::kRowBytes;
+  const int lane = threadIdx.x;
+  const int col = lane % LPT;
+  const int w = blockIdx.x;
+  LineSplit ls;
+  if (!split_line(a.context_lens, a.num_seqs, a.num_q_heads, gridDim.x, w, lane, ls)) return;
+  int h = 0, s = 0;
+  int64_t seg_start = 0;
+  locate_segment(a.context_lens, a.num_seqs, ls.wseq, ls.b0, lane, h, s, seg_start);
+  const int64_t seg_end = seg_start + chunks_of(a.context_lens[s]);
+  if (!(seg_start < ls.b0 && seg_end <= ls.b1)) return;
+  const int64_t wa = worker_of(seg_start, ls.W, ls.NW);
+  float M = -INFINITY, S = 0.f;
+  float O[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) O[e] = 0.f;
+  for (int64_t ww = wa; ww <= w; ++ww) {
+    const int64_t bw = ww * ls.W / ls.NW;
+    const float* P = a.partials + (ww * 2 + (seg_start <= bw ? 0 : 1)) * a.group * (D + 2);
+    const float mp = P[D];
+    const float lp = P[D + 1];
+    const float mn = fmaxf(M, mp);
+    const float fa = fast_exp2(M - mn);
+    const float fb = fast_exp2(mp - mn);
+    S = S * fa + lp * fb;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) O[e] = O[e] * fa + P[col * EPL + e] * fb;
+    M = mn;
+  }
+  char* out_row = static_cast<char*>(a.out) + ((size_t)s * a.num_q_heads + h) * ROW;
+  if (lane < LPT) store_out16<T>(out_row + col * 16, O, 1.f / S);
+}
+
 template <typename T, int D, int BS>
 hipError_t launch_variant(const DecodeArgs* a, int workers, hipStream_t stream, int* resident) {
   if (resident != nullptr) {
@@ -489,6 +555,9 @@ hipError_t launch_variant(const DecodeArgs* a, int workers, hipStream_t stream, 
         resident, reinterpret_cast<const void*>(&decode_valu_kernel<T, D, BS>), 64, 0);
   }
   hipLaunchKernelGGL((decode_valu_kernel<T, D, BS>), dim3(workers), dim3(64), 0, stream, *a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || workers == 1) return e;   // one worker never splits a segment
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(workers), dim3(64), 0, stream, *a);
   return hipGetLastError();
 }
 

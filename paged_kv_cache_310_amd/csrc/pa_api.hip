@@ -174,8 +174,7 @@ int pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, in
     const int st = default_workers_for_current_device(&workers);
     if (st != PA_OK) return st;
   }
-  *bytes = pa::counters_bytes(num_seqs, num_q_heads) +
-           pa::partials_bytes(workers, num_q_heads / num_kv_heads, head_dim);
+  *bytes = pa::partials_bytes(workers, num_q_heads / num_kv_heads, head_dim);
   return PA_OK;
 }
 
@@ -207,8 +206,7 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
     if (st != PA_OK) return st;
   }
   const int group = num_q_heads / num_kv_heads;
-  const size_t need = pa::counters_bytes(num_seqs, num_q_heads) +
-                      pa::partials_bytes(workers, group, head_dim);
+  const size_t need = pa::partials_bytes(workers, group, head_dim);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -248,9 +246,7 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
   a.k_new = k_new;
   a.v_new = v_new;
   a.slot_mapping = slot_mapping;
-  a.counters = static_cast<int*>(workspace);
-  a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        pa::counters_bytes(num_seqs, num_q_heads));
+  a.partials = static_cast<float*>(workspace);
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;

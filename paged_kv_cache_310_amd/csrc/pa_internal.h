@@ -29,7 +29,6 @@ struct DecodeArgs {
   const void* k_new;          // fused append, or nullptr
   const void* v_new;
   const int64_t* slot_mapping;
-  int* counters;              // [num_seqs * num_q_heads] completion counters
   float* partials;            // [workers][2][group][head_dim + 2]
   int64_t max_blocks_per_seq;
   int num_seqs;
@@ -39,11 +38,9 @@ struct DecodeArgs {
   float scale_log2;           // scale * log2(e): scores live in the exp2 domain
 };
 
-// Workspace layout (bytes): counters first, then per-worker partials.
-inline size_t counters_bytes(int num_seqs, int num_q_heads) {
-  size_t b = (size_t)num_seqs * (size_t)num_q_heads * sizeof(int);
-  return (b + 255) & ~(size_t)255;
-}
+// Workspace: per-worker partials, two (max, sum, acc[head_dim]) records per
+// worker and query head of a segment.  Every record is written before it is
+// read in the same call, so the workspace needs no initialisation.
 inline size_t partials_bytes(int workers, int group, int head_dim) {
   return (size_t)workers * 2 * (size_t)group * (size_t)(head_dim + 2) * sizeof(float);
 }

@@ -82,13 +82,35 @@ def test_repeat_runs_are_bitwise_identical():
 
 
 def test_fused_append_equals_separate_append():
+    # Same pools bit for bit; outputs agree to the tolerance (the fused path
+    # adds the newest token in a different fp32 summation order).
     w = small(wl.BF16, 128, 16, 8, 8, seed=13)
     d1, d2 = DeviceWorkload(w), DeviceWorkload(w)
     a = d1.step(fused=True)
     b = d2.step(fused=False)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert_attention_close(out_f64(a), out_f64(b), wl.BF16)
     assert torch.equal(d1.k.view(torch.int16), d2.k.view(torch.int16))
     assert torch.equal(d1.v.view(torch.int16), d2.v.view(torch.int16))
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace, calls of different shapes and worker counts in a row:
+    counters left by one call must never be misread by the next."""
+    import paged_kv_cache_310_amd as pa
+    cases = [small(wl.BF16, 128, 16, 2, 2, seed=31), small(wl.BF16, 128, 16, 40, 40, seed=32),
+             small(wl.BF16, 128, 16, 64, 8, seed=33), small(wl.FP32, 64, 16, 2, 2, seed=34)]
+    workers = [4096, 97, 1000, 64]
+    need = max(pa.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, n)
+               for w, n in zip(cases, workers))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    for round_ in range(2):
+        for i, w in enumerate(cases):
+            dw = DeviceWorkload(w)
+            out = pa.pa_decode(dw.q, dw.k, dw.v, dw.tables, dw.lens, float(w.scale),
+                               k_new=dw.k_new, v_new=dw.v_new, slot_mapping=dw.slots,
+                               workspace=ws, num_workers=workers[i])
+            torch.cuda.synchronize()
+            assert_attention_close(out_f64(out), oracle_decode(w, *oracle_pools(w)), w.dtype)
 
 
 def test_empty_sequences_give_zero_rows():
@@ -253,7 +275,7 @@ def test_workload_tiny_fp32(cache):
     all_rows = [(s, h) for s in range(w.num_seqs) for h in range(w.num_q_heads)]
     a = _check_full(w, fused=True, rows=all_rows)
     b = _check_full(w, fused=False, rows=all_rows)
-    assert torch.equal(a, b)
+    assert_attention_close(out_f64(a), out_f64(b), w.dtype)
 
 
 def test_workload_opt13b_mha(cache):
@@ -266,7 +288,7 @@ def test_workload_llama13b_long(cache):
     w = _full(cache, "llama13b_long")
     a = _check_full(w, fused=True)
     b = _check_full(w, fused=False, compare_pools=False)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert_attention_close(out_f64(a), out_f64(b), w.dtype)
 
 
 def test_workload_shared_prefix_steady(cache):
