@@ -33,7 +33,10 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: achieved HBM GB/s (KV read) & % of peak; seq-steps/sec"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, vendor specification
 DECODE_KERNEL = "decode_valu_kernel"
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_310_amd", "csrc", "decode_kernel.hip")
+# Sources the decode kernel is built from; counter figures taken on other
+# versions of them are not reported.
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_310_amd", "csrc", f)
+                  for f in ("decode_kernel.hip", "decode_common.h", "pa_internal.h")]
 
 
 def log(*a):
@@ -57,7 +60,10 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(workload: str):
@@ -167,11 +173,12 @@ def main():
         if pairs is not None:
             pa.pa_copy_blocks(k, v, pairs)
         if ev is not None:
-            ev[0].record(stream)
+            # the library records these right around the attention kernel
+            pa.pa_set_decode_events(ev[0], ev[1])
         pa.pa_decode(q, k, v, tables, lens, float(w.scale), out=out, k_new=k_new, v_new=v_new,
                      slot_mapping=slots, workspace=workspace, num_workers=args.workers)
         if ev is not None:
-            ev[1].record(stream)
+            pa.pa_set_decode_events(None, None)
 
     for _ in range(args.warmup):
         step()

@@ -87,7 +87,8 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
 
 /* Bytes of device workspace pa_decode needs for these sizes and `num_workers`
  * (0 = the library's default for the current device).  Writes *bytes.  The
- * workspace holds per-worker partial results of the context split:
+ * workspace holds, per worker, a 48-byte merge record (the record array is
+ * padded to 256 bytes) and partial results of the context split:
  * num_workers * 2 * (num_q_heads / num_kv_heads) * (head_dim + 2) floats.
  * It needs no initialisation; one workspace serves successive calls of any
  * shape in stream order (never two calls at once). */
@@ -130,6 +131,14 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
               const void* k_new, const void* v_new, const int64_t* slot_mapping,
               void* workspace, size_t workspace_bytes, int num_workers,
               int dtype, void* stream);
+
+/* Measurement hook.  `before` and `after` are hipEvent_t handles (created by
+ * the caller).  While set, every pa_decode call made from this host thread
+ * records `before` on its stream immediately before launching the attention
+ * kernel and `after` immediately after it -- before the small kernel that
+ * merges split context pieces -- so the attention kernel alone can be timed.
+ * Pass NULL, NULL to stop.  Returns PA_ERR_INVALID if exactly one is NULL. */
+int pa_set_decode_events(void* before, void* after);
 
 /* Static description of a status code (never NULL). */
 const char* pa_status_string(int status);

@@ -8,7 +8,7 @@ host-only modules (block manager, workload generator) import without a GPU.
 """
 
 __all__ = ["pa_append_kv", "pa_copy_blocks", "pa_decode", "pa_decode_workspace_size",
-           "pa_decode_default_workers", "decode_workspace",
+           "pa_decode_default_workers", "decode_workspace", "pa_set_decode_events",
            "pa_status_string", "library_path", "PAError"]
 
 

@@ -65,6 +65,8 @@ def _load():
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i64,
                                   ctypes.c_float, vp, vp, vp, vp, sz, i32, i32, vp]
         lib.pa_decode.restype = i32
+        lib.pa_set_decode_events.argtypes = [vp, vp]
+        lib.pa_set_decode_events.restype = i32
         _lib = lib
         return lib
 
@@ -144,6 +146,20 @@ def pa_decode_default_workers() -> int:
     out = ctypes.c_int(0)
     _call("pa_decode_default_workers", _load().pa_decode_default_workers(ctypes.byref(out)))
     return int(out.value)
+
+
+def pa_set_decode_events(before=None, after=None) -> None:
+    """Record two ``torch.cuda.Event`` objects around the attention kernel of
+    later pa_decode calls on this thread (``None, None`` stops)."""
+    raw = []
+    for ev in (before, after):
+        if ev is None:
+            raw.append(None)
+        else:
+            if ev.cuda_event == 0:          # torch creates the event on first record
+                ev.record()
+            raw.append(ctypes.c_void_p(ev.cuda_event))
+    _call("pa_set_decode_events", _load().pa_set_decode_events(*raw))
 
 
 _workspaces = {}

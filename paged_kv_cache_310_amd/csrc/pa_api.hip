@@ -83,9 +83,20 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int* ou
   return PA_OK;
 }
 
+// Events pa_set_decode_events installed for this host thread.
+thread_local hipEvent_t tl_before = nullptr;
+thread_local hipEvent_t tl_after = nullptr;
+
 }  // namespace
 
 extern "C" {
+
+int pa_set_decode_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return PA_ERR_INVALID;
+  tl_before = static_cast<hipEvent_t>(before);
+  tl_after = static_cast<hipEvent_t>(after);
+  return PA_OK;
+}
 
 const char* pa_status_string(int status) {
   switch (status) {
@@ -246,14 +257,16 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
   a.k_new = k_new;
   a.v_new = v_new;
   a.slot_mapping = slot_mapping;
-  a.partials = static_cast<float*>(workspace);
+  a.records = static_cast<pa::MergeRecord*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pa::records_bytes(workers));
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = group;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return pa::launch_decode(a, dtype, head_dim, block_size, workers, st) == hipSuccess
+  return pa::launch_decode(a, dtype, head_dim, block_size, workers, st, tl_before, tl_after) ==
+                 hipSuccess
              ? PA_OK
              : PA_ERR_HIP;
 }

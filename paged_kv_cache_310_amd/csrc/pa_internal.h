@@ -18,6 +18,20 @@ enum DType : int { kFp32 = 0, kBf16 = 1 };
 
 inline int elem_bytes(int dtype) { return dtype == kBf16 ? 2 : 4; }
 
+// What the merge kernel needs about the split segment a worker closes (the
+// segment holding the worker's first chunk, begun by an earlier worker and
+// ending inside this worker's range).  valid == 0: the worker closes none.
+struct MergeRecord {
+  int64_t W;          // chunks in the line
+  int64_t NW;         // workers with chunks
+  int64_t seg_start;  // first chunk of the segment
+  int64_t first;      // worker holding that chunk
+  int32_t seq, head;
+  int32_t valid, pad;
+};
+
+static_assert(sizeof(MergeRecord) == 48, "merge record layout");
+
 // Everything the decode kernels read, in one POD passed by value.
 struct DecodeArgs {
   void* out;
@@ -29,6 +43,7 @@ struct DecodeArgs {
   const void* k_new;          // fused append, or nullptr
   const void* v_new;
   const int64_t* slot_mapping;
+  MergeRecord* records;       // [workers]
   float* partials;            // [workers][2][group][head_dim + 2]
   int64_t max_blocks_per_seq;
   int num_seqs;
@@ -38,15 +53,22 @@ struct DecodeArgs {
   float scale_log2;           // scale * log2(e): scores live in the exp2 domain
 };
 
-// Workspace: per-worker partials, two (max, sum, acc[head_dim]) records per
-// worker and query head of a segment.  Every record is written before it is
-// read in the same call, so the workspace needs no initialisation.
+// Workspace: one MergeRecord per worker, then per-worker partials, two
+// (max, sum, acc[head_dim]) records per worker and query head of a segment.
+// Everything is written before it is read in the same call, so the
+// workspace needs no initialisation.
+inline size_t records_bytes(int workers) {
+  return ((size_t)workers * sizeof(MergeRecord) + 255) & ~(size_t)255;
+}
 inline size_t partials_bytes(int workers, int group, int head_dim) {
-  return (size_t)workers * 2 * (size_t)group * (size_t)(head_dim + 2) * sizeof(float);
+  return records_bytes(workers) +
+         (size_t)workers * 2 * (size_t)group * (size_t)(head_dim + 2) * sizeof(float);
 }
 
+// Launches the attention kernel (recording `before`/`after`, when not null,
+// around it) and then the merge kernel.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,
-                         int workers, hipStream_t stream);
+                         int workers, hipStream_t stream, hipEvent_t before, hipEvent_t after);
 // Resident decode workers (one-wave workgroups) per CU for a variant.
 hipError_t decode_resident_per_cu(int dtype, int head_dim, int block_size, int* resident);
 hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
@@ -55,8 +77,11 @@ hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const 
 hipError_t launch_copy(void* k_cache, void* v_cache, const int64_t* block_mapping,
                        int64_t num_pairs, int64_t block_bytes, hipStream_t stream);
 
-// Upper bound on decode workers per CU used to size workspaces (4 waves per
-// SIMD); a variant's default is min(this, its resident waves per CU).
-constexpr int kWavesPerCu = 16;
+// Default decode workers per CU (one wave per SIMD).  Measured on the
+// long-context and OPT-shaped batches, 2..16 workers per CU are within 4% of
+// each other (fewer is slightly better: fewer split segments and fewer
+// concurrent streams), while batches that share prefix blocks gain ~25% from
+// 4 over 2, because sharers then run at the same time on one XCD's L2.
+constexpr int kWavesPerCu = 4;
 
 }  // namespace pa

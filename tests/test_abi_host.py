@@ -52,10 +52,11 @@ def test_status_strings(lib):
 
 def test_workspace_size_formula(lib):
     sz = ctypes.c_size_t(0)
+    rec = lambda w: (w * 48 + 255) // 256 * 256     # one 48-byte merge record per worker
     assert lib.pa_decode_workspace_size(32, 40, 40, 128, 4096, ctypes.byref(sz)) == 0
-    assert sz.value == 4096 * 2 * 1 * 130 * 4
+    assert sz.value == rec(4096) + 4096 * 2 * 1 * 130 * 4
     assert lib.pa_decode_workspace_size(256, 64, 8, 128, 100, ctypes.byref(sz)) == 0
-    assert sz.value == 100 * 2 * 8 * 130 * 4
+    assert sz.value == rec(100) + 100 * 2 * 8 * 130 * 4
     assert lib.pa_decode_workspace_size(4, 6, 4, 64, 8, ctypes.byref(sz)) == 1   # 6 % 4 != 0
 
 
@@ -97,6 +98,12 @@ def test_append_and_copy_reject_bad_scalars(lib):
     assert lib.pa_copy_blocks(None, None, None, 0, 10, 8, 16, 128, 1, None) == 0
     assert lib.pa_copy_blocks(FAKE, FAKE, FAKE, 2, 10, 8, 32, 64, 3, None) == 2
     assert lib.pa_copy_blocks(FAKE, FAKE, None, 2, 10, 8, 32, 64, 0, None) == 1
+
+
+def test_decode_event_hook_arguments(lib):
+    assert lib.pa_set_decode_events(FAKE, None) == 1
+    assert lib.pa_set_decode_events(None, FAKE) == 1
+    assert lib.pa_set_decode_events(None, None) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

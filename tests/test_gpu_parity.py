@@ -113,6 +113,25 @@ def test_workspace_reuse_across_shapes():
             assert_attention_close(out_f64(out), oracle_decode(w, *oracle_pools(w)), w.dtype)
 
 
+def test_decode_event_hook_times_the_attention_kernel():
+    import paged_kv_cache_310_amd as pa
+    w = small(wl.BF16, 128, 16, 8, 8, append=False, seed=35)
+    dw = DeviceWorkload(w)
+    outer = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    inner = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    outer[0].record()
+    pa.pa_set_decode_events(inner[0], inner[1])
+    try:
+        out = pa.pa_decode(dw.q, dw.k, dw.v, dw.tables, dw.lens, float(w.scale), num_workers=64)
+    finally:
+        pa.pa_set_decode_events(None, None)
+    outer[1].record()
+    torch.cuda.synchronize()
+    t_in, t_out = inner[0].elapsed_time(inner[1]), outer[0].elapsed_time(outer[1])
+    assert 0 < t_in <= t_out
+    assert_attention_close(out_f64(out), oracle_decode(w, w.k_cache, w.v_cache), wl.BF16)
+
+
 def test_empty_sequences_give_zero_rows():
     lens = [0, 5, 0, 0, 40, 0]
     w = small(wl.BF16, 128, 16, 8, 8, lens=lens, append=False, seed=14)
