@@ -292,11 +292,14 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
 }
 
 // Merges the partial pieces of every segment that spans several workers.
-// One wave per decode worker reads that worker's MergeRecord; the worker
-// that closes a split segment gets its pieces (workers first..w) folded in
-// worker order, which is deterministic, and the output row written.  Runs
-// after the decode launch in stream order, so the partials are visible
-// without any in-kernel fence.
+// One wave per (decode worker, query head of its segment): the wave reads the
+// worker's MergeRecord; for a worker that closes a split segment it folds the
+// pieces of workers first..w for that head and writes the output row.  The
+// pieces' (max, sum) pairs are loaded lane-parallel (64 at a time), so the
+// merge costs a few memory latencies however many pieces a segment has; the
+// fold order is fixed (worker order), so results are deterministic.  Runs
+// after the decode launch in stream order: the partials are visible without
+// any in-kernel fence.
 constexpr int kMergeWaves = 4;   // waves per merge workgroup
 
 template <typename T, int D>
@@ -305,60 +308,75 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   constexpr int LPT = G::kLpt, EPL = G::kEpl, ROW = G::kRowBytes;
   const int lane = threadIdx.x % 64;
   const int col = lane % LPT;
-  const int w = uniform((int)(blockIdx.x * kMergeWaves + threadIdx.x / 64));
+  const int hps = a.heads_per_seg;
+  const int id = uniform((int)(blockIdx.x * kMergeWaves + threadIdx.x / 64));
+  const int w = id / hps;
+  const int g = id - w * hps;
   if (w >= workers) return;
   const MergeRecord r = a.records[w];
   if (!r.valid) return;
-  float M = -INFINITY, S = 0.f;
+  const int64_t npieces = w - r.first + 1;
+  auto piece = [&](int64_t p) {   // partial record of piece p, head g
+    const int64_t ww = r.first + p;
+    const int64_t bw = ww * r.W / r.NW;
+    return a.partials + ((ww * 2 + (r.seg_start <= bw ? 0 : 1)) * a.group + g) * (D + 2);
+  };
+  // Running max over all pieces, then the rescaled sum.
+  float M = -INFINITY;
+  for (int64_t p0 = 0; p0 < npieces; p0 += 64) {
+    const float mp = p0 + lane < npieces ? piece(p0 + lane)[D] : -INFINITY;
+    M = fmaxf(M, mp);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float S = 0.f;
+  for (int64_t p0 = 0; p0 < npieces; p0 += 64) {
+    if (p0 + lane < npieces) {
+      const float* P = piece(p0 + lane);
+      S += P[D + 1] * fast_exp2(P[D] - M);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
   float O[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) O[e] = 0.f;
-  for (int64_t ww = r.first; ww <= w; ++ww) {
-    const int64_t bw = ww * r.W / r.NW;
-    const float* P = a.partials + (ww * 2 + (r.seg_start <= bw ? 0 : 1)) * a.group * (D + 2);
-    const float mp = P[D];
-    const float lp = P[D + 1];
-    const float mn = fmaxf(M, mp);
-    const float fa = fast_exp2(M - mn);
-    const float fb = fast_exp2(mp - mn);
-    S = S * fa + lp * fb;
+  for (int64_t p = 0; p < npieces; ++p) {
+    const float* P = piece(p);
+    const float f = fast_exp2(P[D] - M);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) O[e] = O[e] * fa + P[col * EPL + e] * fb;
-    M = mn;
+    for (int e = 0; e < EPL; ++e) O[e] = fmaf(P[col * EPL + e], f, O[e]);
   }
-  char* out_row = static_cast<char*>(a.out) + ((size_t)r.seq * a.num_q_heads + r.head) * ROW;
+  const int head = r.head * hps + g;
+  char* out_row = static_cast<char*>(a.out) + ((size_t)r.seq * a.num_q_heads + head) * ROW;
   if (lane < LPT) store_out16<T>(out_row + col * 16, O, 1.f / S);
 }
 
-struct Timing {
-  hipEvent_t before, after;
-};
-
 template <typename T, int D, int BS>
-hipError_t launch_variant(const DecodeArgs* a, int workers, hipStream_t stream, int* resident,
-                          const Timing& tm) {
+hipError_t launch_valu(const DecodeArgs* a, int workers, hipStream_t stream, int* resident) {
   if (resident != nullptr) {
     // Resident one-wave workgroups per CU for this variant (occupancy query).
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
         resident, reinterpret_cast<const void*>(&decode_valu_kernel<T, D, BS>), 64, 0);
   }
-  hipError_t e = hipSuccess;
-  if (tm.before != nullptr && (e = hipEventRecord(tm.before, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_valu_kernel<T, D, BS>), dim3(workers), dim3(64), 0, stream, *a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (tm.after != nullptr && (e = hipEventRecord(tm.after, stream)) != hipSuccess) return e;
-  if (workers == 1) return e;   // one worker never splits a segment
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((workers + kMergeWaves - 1) / kMergeWaves),
-                     dim3(64 * kMergeWaves), 0, stream, *a, workers);
   return hipGetLastError();
 }
 
-// Launches the variant, or (resident != nullptr) reports its occupancy.
-hipError_t dispatch(const DecodeArgs* a, int dtype, int head_dim, int block_size, int workers,
-                    hipStream_t stream, int* resident, const Timing& tm) {
+template <typename T, int D>
+hipError_t launch_merge(const DecodeArgs& a, int workers, hipStream_t stream) {
+  const int64_t waves = (int64_t)workers * a.heads_per_seg;
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((waves + kMergeWaves - 1) / kMergeWaves)),
+                     dim3(64 * kMergeWaves), 0, stream, a, workers);
+  return hipGetLastError();
+}
+
+// The vector-ALU attention kernel for one variant, or its occupancy.
+hipError_t dispatch_valu(const DecodeArgs* a, int dtype, int head_dim, int block_size,
+                         int workers, hipStream_t stream, int* resident) {
 #define PA_DISPATCH(T, DT, HD, BSZ)                                          \
   if (dtype == DT && head_dim == HD && block_size == BSZ)                    \
-    return launch_variant<T, HD, BSZ>(a, workers, stream, resident, tm);
+    return launch_valu<T, HD, BSZ>(a, workers, stream, resident);
   PA_DISPATCH(uint16_t, kBf16, 128, 16)
   PA_DISPATCH(uint16_t, kBf16, 128, 32)
   PA_DISPATCH(uint16_t, kBf16, 64, 16)
@@ -371,16 +389,37 @@ hipError_t dispatch(const DecodeArgs* a, int dtype, int head_dim, int block_size
   return hipErrorInvalidValue;
 }
 
-}  // namespace
-
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,
-                         int workers, hipStream_t stream, hipEvent_t before, hipEvent_t after) {
-  return dispatch(&a, dtype, head_dim, block_size, workers, stream, nullptr, Timing{before, after});
+hipError_t dispatch_merge(const DecodeArgs& a, int dtype, int head_dim, int workers,
+                          hipStream_t stream) {
+  if (dtype == kBf16 && head_dim == 128) return launch_merge<uint16_t, 128>(a, workers, stream);
+  if (dtype == kBf16 && head_dim == 64) return launch_merge<uint16_t, 64>(a, workers, stream);
+  if (dtype == kFp32 && head_dim == 128) return launch_merge<float, 128>(a, workers, stream);
+  if (dtype == kFp32 && head_dim == 64) return launch_merge<float, 64>(a, workers, stream);
+  return hipErrorInvalidValue;
 }
 
-hipError_t decode_resident_per_cu(int dtype, int head_dim, int block_size, int* resident) {
-  return dispatch(nullptr, dtype, head_dim, block_size, 0, nullptr, resident,
-                  Timing{nullptr, nullptr});
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& args, int dtype, int head_dim, int block_size,
+                         int workers, hipStream_t stream, hipEvent_t before, hipEvent_t after) {
+  DecodeArgs a = args;
+  const bool mfma = gqa_supported(dtype, head_dim, a.group);
+  a.heads_per_seg = mfma ? a.group : 1;
+  hipError_t e = hipSuccess;
+  if (before != nullptr && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
+  e = mfma ? launch_gqa_attention(a, block_size, workers, stream, nullptr)
+           : dispatch_valu(&a, dtype, head_dim, block_size, workers, stream, nullptr);
+  if (e != hipSuccess) return e;
+  if (after != nullptr && (e = hipEventRecord(after, stream)) != hipSuccess) return e;
+  if (workers == 1) return hipSuccess;   // one worker never splits a segment
+  return dispatch_merge(a, dtype, head_dim, workers, stream);
+}
+
+hipError_t decode_resident_per_cu(int dtype, int head_dim, int block_size, int group,
+                                  int* resident) {
+  if (gqa_supported(dtype, head_dim, group))
+    return launch_gqa_attention(DecodeArgs{}, block_size, 0, nullptr, resident);
+  return dispatch_valu(nullptr, dtype, head_dim, block_size, 0, nullptr, resident);
 }
 
 }  // namespace pa

@@ -71,12 +71,12 @@ int default_workers_for_current_device(int* out) {
 }
 
 // Default workers of one kernel variant: every worker resident at once.
-int default_workers_for_variant(int dtype, int head_dim, int block_size, int* out) {
+int default_workers_for_variant(int dtype, int head_dim, int block_size, int group, int* out) {
   int cus = 0;
   const int st = current_device_cus(&cus);
   if (st != PA_OK) return st;
   int resident = 0;
-  if (pa::decode_resident_per_cu(dtype, head_dim, block_size, &resident) != hipSuccess ||
+  if (pa::decode_resident_per_cu(dtype, head_dim, block_size, group, &resident) != hipSuccess ||
       resident <= 0)
     return PA_ERR_HIP;
   *out = cus * (resident < pa::kWavesPerCu ? resident : pa::kWavesPerCu);
@@ -213,7 +213,8 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
 
   int workers = num_workers;
   if (workers == 0) {
-    const int st = default_workers_for_variant(dtype, head_dim, block_size, &workers);
+    const int st = default_workers_for_variant(dtype, head_dim, block_size,
+                                               num_q_heads / num_kv_heads, &workers);
     if (st != PA_OK) return st;
   }
   const int group = num_q_heads / num_kv_heads;

@@ -50,6 +50,7 @@ struct DecodeArgs {
   int num_q_heads;
   int num_kv_heads;
   int group;                  // num_q_heads / num_kv_heads
+  int heads_per_seg;          // query heads one work segment covers (1, or group on MFMA)
   float scale_log2;           // scale * log2(e): scores live in the exp2 domain
 };
 
@@ -70,7 +71,14 @@ inline size_t partials_bytes(int workers, int group, int head_dim) {
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,
                          int workers, hipStream_t stream, hipEvent_t before, hipEvent_t after);
 // Resident decode workers (one-wave workgroups) per CU for a variant.
-hipError_t decode_resident_per_cu(int dtype, int head_dim, int block_size, int* resident);
+hipError_t decode_resident_per_cu(int dtype, int head_dim, int block_size, int group,
+                                  int* resident);
+// Grouped-query attention on MFMA (gqa_kernel.hip): bf16, head_dim 128,
+// 2 <= group <= 16.  Launches the attention kernel only, or reports its
+// occupancy when resident != nullptr.
+bool gqa_supported(int dtype, int head_dim, int group);
+hipError_t launch_gqa_attention(const DecodeArgs& a, int block_size, int workers,
+                                hipStream_t stream, int* resident);
 hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                          const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
                          int block_size, int row_bytes, hipStream_t stream);

@@ -47,7 +47,10 @@ def _device():
 SHAPES = [(wl.BF16, 128, 16, 8, 8), (wl.BF16, 128, 32, 8, 8), (wl.BF16, 64, 16, 4, 4),
           (wl.BF16, 64, 32, 4, 4), (wl.FP32, 64, 16, 4, 4), (wl.FP32, 64, 32, 4, 4),
           (wl.FP32, 128, 16, 4, 4), (wl.FP32, 128, 32, 2, 2), (wl.BF16, 128, 16, 16, 2),
-          (wl.BF16, 128, 32, 8, 1), (wl.FP32, 64, 16, 8, 2)]
+          (wl.BF16, 128, 32, 8, 1), (wl.FP32, 64, 16, 8, 2),
+          # grouped queries on the matrix-core kernel: groups 2, 3, 4, 16
+          (wl.BF16, 128, 16, 4, 2), (wl.BF16, 128, 32, 6, 2), (wl.BF16, 128, 16, 16, 4),
+          (wl.BF16, 128, 32, 32, 2)]
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
@@ -63,10 +66,11 @@ def test_small_ragged(dtype, d, bs, hq, hkv, fused):
     assert_attention_close(out_f64(out), oracle_decode(w, k_ref, v_ref), dtype)
 
 
+@pytest.mark.parametrize("group", [1, 8])
 @pytest.mark.parametrize("workers", [1, 2, 3, 7, 8, 64, 257, 4096, 100000])
-def test_worker_counts(workers):
-    say("workers", workers)
-    w = small(wl.BF16, 128, 16, 4, 4, seed=11)
+def test_worker_counts(workers, group):
+    say("workers", workers, "group", group)
+    w = small(wl.BF16, 128, 16, 4 * group, 4, seed=11)
     ref = oracle_decode(w, *oracle_pools(w))
     dw = DeviceWorkload(w)
     out = dw.step(fused=True, num_workers=workers)
