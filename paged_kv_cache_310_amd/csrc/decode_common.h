@@ -17,6 +17,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // space so that wave-uniform reads become scalar loads: they are counted by
 // lgkmcnt, so waiting for a table entry never waits for in-flight tile loads.
 typedef const int32_t __attribute__((address_space(4))) const_i32;
+typedef const int64_t __attribute__((address_space(4))) const_i64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource for one tile: scalar 48-bit base, byte range [0, bytes).
@@ -238,6 +239,60 @@ __device__ __forceinline__ void locate_segment(const int32_t* lens, int num_seqs
   int64_t before = 0;
   locate_sequence(lens, num_seqs, c - (int64_t)h * wseq, lane, s, before);
   seg_start = (int64_t)h * wseq + before;
+}
+
+// Wave-uniform cursor over the chunk line: chunk c is chunk j (of n) of the
+// segment (head h, sequence s of length L) that starts at line chunk
+// seg_start.
+struct Cursor {
+  int64_t c;
+  int64_t seg_start;
+  int h, s, L, n, j;
+};
+
+// Moves the cursor to the next chunk of the line, skipping empty sequences.
+// Callers never move it past the last chunk of their range.
+__device__ __forceinline__ void cursor_next(Cursor& k, const int32_t* lens_ptr, int num_seqs) {
+  const const_i32* lens = (const const_i32*)lens_ptr;   // scalar loads (lgkmcnt)
+  ++k.c;
+  if (++k.j < k.n) return;
+  do {
+    if (++k.s == num_seqs) {
+      k.s = 0;
+      ++k.h;
+    }
+    k.L = lens[k.s];
+  } while (k.L == 0);
+  k.n = chunks_of(k.L);
+  k.j = 0;
+  k.seg_start = k.c;
+}
+
+// What a tile carries about its chunk, so the consumer can switch segments
+// without draining the load pipeline.
+struct ChunkMeta {
+  int64_t seg_start;
+  int64_t slot;      // fused append into this segment's last chunk (< 0: none)
+  int h, s, L, n, j;
+  bool first;        // first chunk of the segment in this worker's range
+  bool last;         // last chunk of the segment in this worker's range
+};
+
+__device__ __forceinline__ ChunkMeta chunk_meta(const Cursor& k, int64_t b0, int64_t b1,
+                                               const int64_t* slot_mapping) {
+  ChunkMeta m;
+  m.seg_start = k.seg_start;
+  m.h = k.h;
+  m.s = k.s;
+  m.L = k.L;
+  m.n = k.n;
+  m.j = k.j;
+  m.first = k.c == b0 || k.j == 0;
+  m.last = k.c == b1 - 1 || k.j == k.n - 1;
+  m.slot = (slot_mapping != nullptr && k.j == k.n - 1)
+               ? ((const const_i64*)slot_mapping)[k.s]   // scalar load (lgkmcnt)
+               : -1;
+  return m;
 }
 
 }  // namespace dev

@@ -53,10 +53,11 @@ struct Tile {
   u32x4 v[Geo<T, D>::kNl];
 };
 
-// Minimum waves per SIMD the register budget is sized for: two 16-token tiles
-// in flight cost 2 * 2 * NL * 4 VGPRs, so the 8 KiB tiles of fp32 d128 get 2.
+// Register budget: at least 2 waves per SIMD (256 VGPRs).  The default is
+// one worker per SIMD, so the budget goes to keeping two tiles, the segment's
+// q and the fused-append row in registers rather than to occupancy.
 template <typename T, int D>
-constexpr int min_waves() { return Geo<T, D>::kNl >= 8 ? 2 : 4; }
+constexpr int min_waves() { return 2; }
 
 template <typename T, int D, int BS>
 __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(const DecodeArgs a) {
@@ -91,156 +92,143 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     return;
   }
   const int64_t b0 = ls.b0, b1 = ls.b1;
-  int h = 0, s = 0;
-  int64_t seg_start = 0;
-  locate_segment(lens, B, ls.wseq, b0, lane, h, s, seg_start);
-  int L = lens[s];
-  int n = chunks_of(L);
-  int64_t c = b0;
+  Cursor cur;
+  cur.c = b0;
+  locate_segment(lens, B, ls.wseq, b0, lane, cur.h, cur.s, cur.seg_start);
+  cur.L = lens[cur.s];
+  cur.n = chunks_of(cur.L);
+  cur.j = (int)(b0 - cur.seg_start);
   if (lane == 0) {
     // This worker closes the split segment holding b0 if the segment began
     // in an earlier worker and ends inside this range.
     MergeRecord r;
     r.W = ls.W;
     r.NW = ls.NW;
-    r.seg_start = seg_start;
-    r.first = worker_of(seg_start, ls.W, ls.NW);
-    r.seq = s;
-    r.head = h;
-    r.valid = (seg_start < b0 && seg_start + n <= b1) ? 1 : 0;
+    r.seg_start = cur.seg_start;
+    r.first = worker_of(cur.seg_start, ls.W, ls.NW);
+    r.seq = cur.s;
+    r.head = cur.h;
+    r.valid = (cur.seg_start < b0 && cur.seg_start + cur.n <= b1) ? 1 : 0;
     r.pad = 0;
     a.records[w] = r;
   }
 
   const int64_t block_stride = (int64_t)HKV * BS * ROW;
+  auto table_of = [&](const Cursor& k) {
+    return (const const_i32*)(a.block_tables + (int64_t)k.s * a.max_blocks_per_seq);
+  };
+  // Physical block of the chunk under the cursor, read one chunk ahead.
+  int next_pb = table_of(cur)[cur.j / CPB];
 
-  for (;;) {
-    const int64_t seg_end = seg_start + n;
-    const int64_t piece_end = seg_end < b1 ? seg_end : b1;
-    const int j0 = (int)(c - seg_start);
-    const int j1 = (int)(piece_end - seg_start);
+  struct Tile {
+    u32x4 k[NL], v[NL];
+    u32x4 q;        // valid when meta.first
+    u32x4 kn, vn;   // valid when meta.slot >= 0 (the newest token of the segment)
+    ChunkMeta meta;
+  };
 
-    // ---------------------------------------------------------------- piece
-    const int kvh = h / a.group;
-    const u32x4 qv = load16(tile_rsrc(static_cast<const char*>(a.q) + ((size_t)s * HQ + h) * ROW, ROW),
-                            col * 16);
-    // Fused append: the worker holding the segment's last chunk owns position
-    // L-1.  It masks that position in the pooled tiles, folds the token in from
-    // k_new/v_new after the chunk loop and stores it to its slot, so the loop
-    // itself has no conditional loads or stores.
-    int64_t slot = -1;
-    if (a.slot_mapping != nullptr && j1 == n) slot = a.slot_mapping[s];
-    const bool app = slot >= 0;
-    const int L_pool = app ? L - 1 : L;   // positions read from the pool
-    u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
-    if (app) {
-      const char* knew = static_cast<const char*>(a.k_new) + ((size_t)s * HKV + kvh) * ROW;
-      const char* vnew = static_cast<const char*>(a.v_new) + ((size_t)s * HKV + kvh) * ROW;
-      kn = load16(tile_rsrc(knew, ROW), col * 16);
-      vn = load16(tile_rsrc(vnew, ROW), col * 16);
+  // Loads the chunk under the cursor, then moves the cursor (unless it is on
+  // the range's last chunk) and prefetches the next chunk's block number.
+  auto issue = [&](Tile& t) {
+    t.meta = chunk_meta(cur, b0, b1, a.slot_mapping);
+    const int kvh = cur.h / a.group;
+    const int64_t off = (int64_t)next_pb * block_stride + (int64_t)kvh * BS * ROW +
+                        (int64_t)(cur.j % CPB) * kChunk * ROW;
+    const __amdgpu_buffer_rsrc_t kr =
+        tile_rsrc(static_cast<const char*>(a.k_cache) + off, kChunk * ROW);
+    const __amdgpu_buffer_rsrc_t vr =
+        tile_rsrc(static_cast<const char*>(a.v_cache) + off, kChunk * ROW);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      t.k[i] = load16(kr, i * 1024 + lane * 16);
+      t.v[i] = load16(vr, i * 1024 + lane * 16);
     }
-
-    const const_i32* tab =
-        (const const_i32*)(a.block_tables + (int64_t)s * a.max_blocks_per_seq);
-    const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * BS * ROW;
-    const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * BS * ROW;
-
-    // Physical block of the next chunk to issue, read one chunk ahead.
-    int next_pb = tab[j0 / CPB];
-
-    float m = -INFINITY, l = 0.f;
-    float o[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-
-    auto issue = [&](Tile<T, D>& t, int j) {
-      const int pb = next_pb;
-      next_pb = tab[(j + 1 < j1 ? j + 1 : j) / CPB];
-      const int64_t off = (int64_t)pb * block_stride + (int64_t)(j % CPB) * kChunk * ROW;
-      const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + off, kChunk * ROW);
-      const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + off, kChunk * ROW);
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        t.k[i] = load16(kr, i * 1024 + lane * 16);
-        t.v[i] = load16(vr, i * 1024 + lane * 16);
-      }
-      // Keep the loads ahead of the math on the other tile.
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    auto consume = [&](const Tile<T, D>& t, int j) {
-      float sc[NL];
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const float dot = row_sum<LPT>(dot16<T>(qv, t.k[i]));
-        const int tok = j * kChunk + i * TPL + trow;
-        sc[i] = tok < L_pool ? dot * a.scale_log2 : -INFINITY;
-      }
-      float mx = sc[0];
-#pragma unroll
-      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[i]);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      l *= alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const float p = fast_exp2(sc[i] - m_use);
-        l += p;
-        const bool ok = j * kChunk + i * TPL + trow < L_pool;
-        const u32x4 vv = ok ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
-        axpy16<T>(o, p, vv);
-      }
-      m = m_new;
-    };
-
-    // Two tiles in ping-pong: the loads of one are in flight while the other
-    // is consumed (no register copies, so no wait on the in-flight loads).
-    // The steady-state loop issues unconditionally, so every path into a
-    // consume has the same loads in flight and the compiler waits only for
-    // the tile being consumed; the last one or two chunks are peeled.
-    Tile<T, D> ta, tb;
-    issue(ta, j0);
-    int j = j0;
-    for (; j + 2 < j1; j += 2) {
-      issue(tb, j + 1);
-      consume(ta, j);
-      issue(ta, j + 2);
-      consume(tb, j + 1);
+    if (t.meta.first)
+      t.q = load16(tile_rsrc(static_cast<const char*>(a.q) + ((size_t)cur.s * HQ + cur.h) * ROW,
+                             ROW), col * 16);
+    if (t.meta.slot >= 0) {
+      const size_t row = ((size_t)cur.s * HKV + kvh) * ROW;
+      t.kn = load16(tile_rsrc(static_cast<const char*>(a.k_new) + row, ROW), col * 16);
+      t.vn = load16(tile_rsrc(static_cast<const char*>(a.v_new) + row, ROW), col * 16);
     }
-    if (j + 1 < j1) {
-      issue(tb, j + 1);
-      consume(ta, j);
-      consume(tb, j + 1);
-    } else {
-      consume(ta, j);
+    // Keep the loads ahead of the math on the other tile.
+    __builtin_amdgcn_sched_barrier(0);
+    if (cur.c + 1 < b1) {
+      cursor_next(cur, lens, B);
+      next_pb = table_of(cur)[cur.j / CPB];
     }
+  };
 
-    if (app) {
-      // The newest token joins token row 0; its K/V row goes to its slot.
-      const float dot = row_sum<LPT>(dot16<T>(qv, kn));
+  // Consumer state of the segment being accumulated.
+  u32x4 qv = {0u, 0u, 0u, 0u};
+  float m = -INFINITY, l = 0.f;
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+
+  auto consume = [&](const Tile& t) {
+    const ChunkMeta& mt = t.meta;
+    if (mt.first) {
+      qv = t.q;
+      m = -INFINITY;
+      l = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+    }
+    // The newest token's pool slot is stale in a fused append: mask it here
+    // and add the token from k_new/v_new below.
+    const int L_pool = mt.slot >= 0 ? mt.L - 1 : mt.L;
+    const int tok0 = mt.j * kChunk + trow;
+    float sc[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float dot = row_sum<LPT>(dot16<T>(qv, t.k[i]));
+      sc[i] = tok0 + i * TPL < L_pool ? dot * a.scale_log2 : -INFINITY;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[i]);
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float p = fast_exp2(sc[i] - m_use);
+      l += p;
+      const u32x4 vv = tok0 + i * TPL < L_pool ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
+      axpy16<T>(o, p, vv);
+    }
+    m = m_new;
+    if (!mt.last) return;
+
+    // ---- end of this worker's part of the segment
+    const int kvh = mt.h / a.group;
+    if (mt.slot >= 0) {
+      // The newest token joins token row 0; its K/V row goes to its slot
+      // (written once per KV head, by the group's first query head).
+      const float dot = row_sum<LPT>(dot16<T>(qv, t.kn));
       if (trow == 0) {
-        const float sc = dot * a.scale_log2;
-        const float m_new = fmaxf(m, sc);
-        const float alpha = fast_exp2(m - m_new);
-        const float p = fast_exp2(sc - m_new);
-        l = l * alpha + p;
+        const float s_new = dot * a.scale_log2;
+        const float mm = fmaxf(m, s_new);
+        const float al = fast_exp2(m - mm);
+        const float p = fast_exp2(s_new - mm);
+        l = l * al + p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] *= alpha;
-        axpy16<T>(o, p, vn);
-        m = m_new;
-        if (h % a.group == 0) {
-          const int64_t blk = slot / BS;
-          const int64_t pos = slot - blk * BS;
+        for (int e = 0; e < EPL; ++e) o[e] *= al;
+        axpy16<T>(o, p, t.vn);
+        m = mm;
+        if (mt.h % a.group == 0) {
+          const int64_t blk = mt.slot / BS;
+          const int64_t pos = mt.slot - blk * BS;
           const int64_t row_off = ((blk * HKV + kvh) * BS + pos) * ROW + col * 16;
-          *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) + row_off) = kn;
-          *reinterpret_cast<u32x4*>(static_cast<char*>(a.v_cache) + row_off) = vn;
+          *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) + row_off) = t.kn;
+          *reinterpret_cast<u32x4*>(static_cast<char*>(a.v_cache) + row_off) = t.vn;
         }
       }
     }
-
     // Merge the token rows of the wavefront (lanes with equal col).
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
@@ -258,14 +246,14 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
       }
       m = mm;
     }
-
-    char* out_row = static_cast<char*>(a.out) + ((size_t)s * HQ + h) * ROW;
-    if (j0 == 0 && j1 == n) {
+    const bool whole = mt.seg_start >= b0 && mt.seg_start + mt.n <= b1;
+    if (whole) {
+      char* out_row = static_cast<char*>(a.out) + ((size_t)mt.s * HQ + mt.h) * ROW;
       if (lane < LPT) store_out16<T>(out_row + col * 16, o, 1.f / l);
     } else {
-      // Partial piece: publish (max, sum, acc); the merge kernel, which runs
-      // after this launch, combines the pieces of the segment.
-      const int which = seg_start <= b0 ? 0 : 1;
+      // Partial piece: publish (max, sum, acc); the merge kernel combines
+      // the pieces after this launch.
+      const int which = mt.seg_start <= b0 ? 0 : 1;
       float* P = a.partials + ((int64_t)w * 2 + which) * a.group * (D + 2);
       if (lane < LPT) {
 #pragma unroll
@@ -276,18 +264,27 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
         P[D + 1] = l;
       }
     }
-    // ------------------------------------------------------------ next piece
-    c = piece_end;
-    if (c >= b1) break;
-    do {
-      if (++s == B) {
-        s = 0;
-        ++h;
-      }
-      L = lens[s];
-    } while (L == 0);
-    n = chunks_of(L);
-    seg_start = c;
+  };
+
+  // Two tiles in ping-pong over the whole range: the steady-state loop issues
+  // unconditionally, so every path into a consume has the same tile loads in
+  // flight, and segment switches never drain the pipeline.
+  const int64_t count = b1 - b0;
+  Tile ta, tb;
+  issue(ta);
+  int64_t i = 0;
+  for (; i + 2 < count; i += 2) {
+    issue(tb);
+    consume(ta);
+    issue(ta);
+    consume(tb);
+  }
+  if (i + 1 < count) {
+    issue(tb);
+    consume(ta);
+    consume(tb);
+  } else {
+    consume(ta);
   }
 }
 

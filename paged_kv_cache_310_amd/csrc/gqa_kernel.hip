@@ -28,7 +28,7 @@
 //    l%16 = n, its running max agreed on with two permlane swaps per chunk.
 //    P is rounded to bf16 for the MFMA, and the softmax sum adds the same
 //    rounded weights, so numerator and denominator stay consistent.
-// The work split, table walk, pipelining, fused append and partial pieces
+// The work split, cross-segment pipeline, fused append and partial pieces
 // follow the vector kernel (decode_kernel.hip).
 #include "decode_common.h"
 
@@ -47,11 +47,6 @@ constexpr int kTile = kChunk * kRow;         // 4 KiB
 
 // Token (within the chunk) of MFMA row / k-index m.
 __device__ __forceinline__ int token_of(int m) { return 4 * (m & 3) + (m >> 2); }
-
-struct GqaTile {
-  u32x4 k[4];   // K operand pieces: token token_of(l%16), dims 32c + 8(l/16)
-  u32x4 v[4];   // V rows: load i = token 4i + l/16, dims 8(l%16)..+8
-};
 
 // Sum (or max) of a value over the four lanes that share l%16.
 __device__ __forceinline__ float group4_sum(float x) {
@@ -102,181 +97,165 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
     return;
   }
   const int64_t b0 = ls.b0, b1 = ls.b1;
-  int h = 0, s = 0;
-  int64_t seg_start = 0;
-  locate_segment(lens, B, ls.wseq, b0, lane, h, s, seg_start);
-  int L = lens[s];
-  int nch = chunks_of(L);
-  int64_t c = b0;
+  Cursor cur;
+  cur.c = b0;
+  locate_segment(lens, B, ls.wseq, b0, lane, cur.h, cur.s, cur.seg_start);
+  cur.L = lens[cur.s];
+  cur.n = chunks_of(cur.L);
+  cur.j = (int)(b0 - cur.seg_start);
   if (lane == 0) {
     MergeRecord r;
     r.W = ls.W;
     r.NW = ls.NW;
-    r.seg_start = seg_start;
-    r.first = worker_of(seg_start, ls.W, ls.NW);
-    r.seq = s;
-    r.head = h;
-    r.valid = (seg_start < b0 && seg_start + nch <= b1) ? 1 : 0;
+    r.seg_start = cur.seg_start;
+    r.first = worker_of(cur.seg_start, ls.W, ls.NW);
+    r.seq = cur.s;
+    r.head = cur.h;
+    r.valid = (cur.seg_start < b0 && cur.seg_start + cur.n <= b1) ? 1 : 0;
     r.pad = 0;
     a.records[w] = r;
   }
 
   const int64_t block_stride = (int64_t)HKV * BS * kRow;
   const bool real_head = n < G;
+  const int krow_off = token_of(n) * kRow + g4 * 16;
+  auto table_of = [&](const Cursor& k) {
+    return (const const_i32*)(a.block_tables + (int64_t)k.s * a.max_blocks_per_seq);
+  };
+  int next_pb = table_of(cur)[cur.j / CPB];
 
-  for (;;) {
-    const int64_t seg_end = seg_start + nch;
-    const int64_t piece_end = seg_end < b1 ? seg_end : b1;
-    const int j0 = (int)(c - seg_start);
-    const int j1 = (int)(piece_end - seg_start);
-    const int kvh = h;
-    const int hq0 = kvh * G;
+  struct Tile {
+    u32x4 k[4];            // K operand: token token_of(l%16), dims 32c + 8(l/16)
+    u32x4 v[4];            // V rows: load i = token 4i + l/16, dims 8(l%16)..+8
+    u32x4 q[4];            // Q^T operand of the segment, valid when meta.first
+    ChunkMeta meta;
+  };
 
-    // Q^T operand: head n of the group, dims 32c + 8*g4 .. +8 (zero padding heads).
-    u32x4 qf[4];
-    {
-      const char* qrow = static_cast<const char*>(a.q) +
-                         ((size_t)s * HQ + hq0 + (real_head ? n : 0)) * kRow + g4 * 16;
+  auto issue = [&](Tile& t) {
+    t.meta = chunk_meta(cur, b0, b1, a.slot_mapping);
+    const int64_t off = (int64_t)next_pb * block_stride + (int64_t)cur.h * BS * kRow +
+                        (int64_t)(cur.j % CPB) * kTile;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(static_cast<const char*>(a.k_cache) + off, kTile);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(static_cast<const char*>(a.v_cache) + off, kTile);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + k * 64);
-        qf[k] = real_head ? x : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int k = 0; k < 4; ++k) t.k[k] = load16(kr, krow_off + k * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.v[i] = load16(vr, i * 1024 + lane * 16);
+    if (t.meta.first) {
+      // head n of the group, dims 32k + 8*g4 .. +8 (padding heads read head 0, zeroed later)
+      const __amdgpu_buffer_rsrc_t qr = tile_rsrc(
+          static_cast<const char*>(a.q) + ((size_t)cur.s * HQ + cur.h * G) * kRow, G * kRow);
+      const int qoff = (real_head ? n : 0) * kRow + g4 * 16;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t.q[k] = load16(qr, qoff + k * 64);
     }
-
-    int64_t slot = -1;
-    if (a.slot_mapping != nullptr && j1 == nch) slot = a.slot_mapping[s];
-    const bool app = slot >= 0;
-    const int L_pool = app ? L - 1 : L;
-
-    const const_i32* tab =
-        (const const_i32*)(a.block_tables + (int64_t)s * a.max_blocks_per_seq);
-    const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)kvh * BS * kRow;
-    const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)kvh * BS * kRow;
-    int next_pb = tab[j0 / CPB];
-
-    float m = -INFINITY, l = 0.f;
-    f32x4_t o[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const int krow_off = token_of(n) * kRow + g4 * 16;
-
-    auto issue = [&](GqaTile& t, int j) {
-      const int pb = next_pb;
-      next_pb = tab[(j + 1 < j1 ? j + 1 : j) / CPB];
-      const int64_t off = (int64_t)pb * block_stride + (int64_t)(j % CPB) * kTile;
-      const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kbase + off, kTile);
-      const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vbase + off, kTile);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) t.k[k] = load16(kr, krow_off + k * 64);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t.v[i] = load16(vr, i * 1024 + lane * 16);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    auto consume = [&](const GqaTile& t, int j) {
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[k]),
-                                                        __builtin_bit_cast(bf16x8_t, qf[k]),
-                                                        sacc, 0, 0, 0);
-      const int base = j * kChunk + g4;   // lane holds tokens base + 4i
-      float sc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = base + 4 * i < L_pool ? sacc[i] * a.scale_log2 : -INFINITY;
-      const float mx = group4_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      if (__ballot(alpha != 1.f)) {       // rescale only when some running max moved
-        l *= alpha;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] *= alpha;
-      }
-      m = m_new;
-      // P^T operand: the four weights of this lane, rounded to bf16.
-      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-      bf16x4_t pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = (__bf16)fast_exp2(sc[i] - m_use);
-        l += (float)pb[i];
-      }
-      const i16x4_t pop = __builtin_bit_cast(i16x4_t, pb);
-      // V rows of masked tokens are zeroed (a NaN in slack must not reach O).
-      u32x4 v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = base + 4 * i < L_pool ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
-        const int dw = k >> 1;
-        i16x4_t va;
-        const uint32_t lo = __builtin_amdgcn_perm(v[1][dw], v[0][dw], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(v[3][dw], v[2][dw], sel);
-        va = __builtin_bit_cast(i16x4_t, (uint64_t)lo | ((uint64_t)hi << 32));
-        o[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pop, o[k], 0, 0, 0);
-      }
-    };
-
-    GqaTile ta, tb;
-    issue(ta, j0);
-    int j = j0;
-    for (; j + 2 < j1; j += 2) {
-      issue(tb, j + 1);
-      consume(ta, j);
-      issue(ta, j + 2);
-      consume(tb, j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (cur.c + 1 < b1) {
+      cursor_next(cur, lens, B);
+      next_pb = table_of(cur)[cur.j / CPB];
     }
-    if (j + 1 < j1) {
-      issue(tb, j + 1);
-      consume(ta, j);
-      consume(tb, j + 1);
-    } else {
-      consume(ta, j);
-    }
+  };
 
+  u32x4 qf[4];
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o[8];
+
+  auto consume = [&](const Tile& t) {
+    const ChunkMeta& mt = t.meta;
+    if (mt.first) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qf[k] = real_head ? t.q[k] : u32x4{0u, 0u, 0u, 0u};
+      m = -INFINITY;
+      l = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int L_pool = mt.slot >= 0 ? mt.L - 1 : mt.L;
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[k]),
+                                                      __builtin_bit_cast(bf16x8_t, qf[k]),
+                                                      sacc, 0, 0, 0);
+    const int base = mt.j * kChunk + g4;   // lane holds tokens base + 4i
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = base + 4 * i < L_pool ? sacc[i] * a.scale_log2 : -INFINITY;
+    const float mx = group4_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    if (__ballot(alpha != 1.f)) {       // rescale only when some running max moved
+      l *= alpha;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] *= alpha;
+    }
+    m = m_new;
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    bf16x4_t pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pb[i] = (__bf16)fast_exp2(sc[i] - m_use);
+      l += (float)pb[i];
+    }
+    const i16x4_t pop = __builtin_bit_cast(i16x4_t, pb);
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = base + 4 * i < L_pool ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+      const int dw = k >> 1;
+      const uint32_t lo = __builtin_amdgcn_perm(v[1][dw], v[0][dw], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(v[3][dw], v[2][dw], sel);
+      const i16x4_t va = __builtin_bit_cast(i16x4_t, (uint64_t)lo | ((uint64_t)hi << 32));
+      o[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pop, o[k], 0, 0, 0);
+    }
+    if (!mt.last) return;
+
+    // ---- end of this worker's part of the segment
     l = group4_sum(l);   // every lane of head n now holds the head's full sum
-
-    if (app) {
-      // Newest token from k_new/v_new: score q.k_new for head n over the
-      // lane's 32 dims of qf, summed over the four lanes of the head.
-      const char* knew = static_cast<const char*>(a.k_new) + ((size_t)s * HKV + kvh) * kRow;
-      const char* vnew = static_cast<const char*>(a.v_new) + ((size_t)s * HKV + kvh) * kRow;
+    if (mt.slot >= 0) {
+      // The newest token's rows, read here (once per appended segment).
+      const size_t row = ((size_t)mt.s * HKV + mt.h) * kRow;
+      const __amdgpu_buffer_rsrc_t knr = tile_rsrc(static_cast<const char*>(a.k_new) + row, kRow);
+      const __amdgpu_buffer_rsrc_t vnr = tile_rsrc(static_cast<const char*>(a.v_new) + row, kRow);
+      u32x4 kn[4], vn[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kn[k] = load16(knr, k * 64 + g4 * 16);   // dims 32k + 8*g4
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vn[i] = load16(vnr, g4 * 64 + i * 16);   // dims 32*g4 + 8i
       float d = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4 kk = *reinterpret_cast<const u32x4*>(knew + k * 64 + g4 * 16);
-        d = dot16<uint16_t>(qf[k], kk) + d;
-      }
-      const float sc = group4_sum(d) * a.scale_log2;
-      const float m_new = fmaxf(m, sc);
-      const float alpha = fast_exp2(m - m_new);
-      const float p = fast_exp2(sc - m_new);
-      l = l * alpha + p;
+      for (int k = 0; k < 4; ++k) d = dot16<uint16_t>(qf[k], kn[k]) + d;
+      const float s_new = group4_sum(d) * a.scale_log2;
+      const float mm = fmaxf(m, s_new);
+      const float al = fast_exp2(m - mm);
+      const float p = fast_exp2(s_new - mm);
+      l = l * al + p;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(vnew + (g4 * 32 + i * 8) * 2);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k][i] = fmaf(p, bf16_elem(vv, k), o[k][i] * alpha);
+        for (int k = 0; k < 8; ++k) o[k][i] = fmaf(p, bf16_elem(vn[i], k), o[k][i] * al);
       }
-      m = m_new;
-      if (lane < kRow / 16) {
-        const int64_t blk = slot / BS;
-        const int64_t pos = slot - blk * BS;
-        const int64_t row_off = ((blk * HKV + kvh) * BS + pos) * kRow + lane * 16;
-        *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) + row_off) =
-            *reinterpret_cast<const u32x4*>(knew + lane * 16);
-        *reinterpret_cast<u32x4*>(static_cast<char*>(a.v_cache) + row_off) =
-            *reinterpret_cast<const u32x4*>(vnew + lane * 16);
+      m = mm;
+      if (n == 0) {
+        // lanes 0, 16, 32, 48 hold every 16-byte piece of both rows
+        const int64_t blk = mt.slot / BS;
+        const int64_t pos = mt.slot - blk * BS;
+        char* krow = static_cast<char*>(a.k_cache) + ((blk * HKV + mt.h) * BS + pos) * kRow;
+        char* vrow = static_cast<char*>(a.v_cache) + ((blk * HKV + mt.h) * BS + pos) * kRow;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          *reinterpret_cast<u32x4*>(krow + k * 64 + g4 * 16) = kn[k];
+          *reinterpret_cast<u32x4*>(vrow + g4 * 64 + k * 16) = vn[k];
+        }
       }
     }
-
     if (real_head) {
-      if (j0 == 0 && j1 == nch) {
-        char* orow = static_cast<char*>(a.out) + ((size_t)s * HQ + hq0 + n) * kRow + g4 * 64;
+      const bool whole = mt.seg_start >= b0 && mt.seg_start + mt.n <= b1;
+      if (whole) {
+        char* orow = static_cast<char*>(a.out) + ((size_t)mt.s * HQ + mt.h * G + n) * kRow + g4 * 64;
         const float inv = 1.f / l;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -286,7 +265,7 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
           store_out16<uint16_t>(orow + i * 16, vals, inv);
         }
       } else {
-        const int which = seg_start <= b0 ? 0 : 1;
+        const int which = mt.seg_start <= b0 ? 0 : 1;
         float* P = a.partials + (((int64_t)w * 2 + which) * G + n) * (kD + 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -299,18 +278,24 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
         }
       }
     }
+  };
 
-    c = piece_end;
-    if (c >= b1) break;
-    do {
-      if (++s == B) {
-        s = 0;
-        ++h;
-      }
-      L = lens[s];
-    } while (L == 0);
-    nch = chunks_of(L);
-    seg_start = c;
+  const int64_t count = b1 - b0;
+  Tile ta, tb;
+  issue(ta);
+  int64_t i = 0;
+  for (; i + 2 < count; i += 2) {
+    issue(tb);
+    consume(ta);
+    issue(ta);
+    consume(tb);
+  }
+  if (i + 1 < count) {
+    issue(tb);
+    consume(ta);
+    consume(tb);
+  } else {
+    consume(ta);
   }
 }
 
