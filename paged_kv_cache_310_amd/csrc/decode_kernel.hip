@@ -106,10 +106,10 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     r.NW = ls.NW;
     r.seg_start = cur.seg_start;
     r.first = worker_of(cur.seg_start, ls.W, ls.NW);
+    r.first_slot = cur.seg_start > r.first * ls.W / ls.NW ? 1 : 0;
     r.seq = cur.s;
     r.head = cur.h;
     r.valid = (cur.seg_start < b0 && cur.seg_start + cur.n <= b1) ? 1 : 0;
-    r.pad = 0;
     a.records[w] = r;
   }
 
@@ -253,15 +253,16 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     } else {
       // Partial piece: publish (max, sum, acc); the merge kernel combines
       // the pieces after this launch.
-      const int which = mt.seg_start <= b0 ? 0 : 1;
-      float* P = a.partials + ((int64_t)w * 2 + which) * a.group * (D + 2);
+      const int64_t slot = ((int64_t)w * 2 + (mt.seg_start <= b0 ? 0 : 1)) * a.group;
       if (lane < LPT) {
+        float* acc = a.partials + slot * D + col * EPL;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) P[col * EPL + e] = o[e];
+        for (int e = 0; e < EPL; ++e) acc[e] = o[e];
       }
       if (lane == 0) {
-        P[D] = m;
-        P[D + 1] = l;
+        float* pair = a.partials + partial_pairs_offset(nworkers, a.group, D) + slot * 2;
+        pair[0] = m;
+        pair[1] = l;
       }
     }
   };
@@ -289,64 +290,100 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
 }
 
 // Merges the partial pieces of every segment that spans several workers.
-// One wave per (decode worker, query head of its segment): the wave reads the
-// worker's MergeRecord; for a worker that closes a split segment it folds the
-// pieces of workers first..w for that head and writes the output row.  The
-// pieces' (max, sum) pairs are loaded lane-parallel (64 at a time), so the
-// merge costs a few memory latencies however many pieces a segment has; the
-// fold order is fixed (worker order), so results are deterministic.  Runs
-// after the decode launch in stream order: the partials are visible without
-// any in-kernel fence.
+// One wave per (decode worker, group of kMergeHeads query heads of its
+// segment); each lane owns 4 dims of one head.  A worker that closes a split
+// segment (its MergeRecord is valid) folds the pieces of workers first..w in
+// worker order, 8 pieces per batch: the batch's accumulator rows and (max,
+// sum) pairs are all loaded before any is used, with a running max across
+// batches, so a segment of up to 8 pieces costs one memory latency after the
+// record.  The fold order is fixed, so results are deterministic.  Runs after
+// the decode launch in stream order: the partials are visible without any
+// in-kernel fence.
 constexpr int kMergeWaves = 4;   // waves per merge workgroup
+constexpr int kMergeBatch = 8;   // pieces loaded together
+
+template <int D>
+constexpr int merge_heads_per_wave() { return 64 / (D / 4); }
+
+template <typename T>
+__device__ __forceinline__ void store_out4(void* dst, const float* o, float inv);
+
+template <>
+__device__ __forceinline__ void store_out4<uint16_t>(void* dst, const float* o, float inv) {
+  uint2 r;
+  r.x = f32_to_bf16(o[0] * inv) | (f32_to_bf16(o[1] * inv) << 16);
+  r.y = f32_to_bf16(o[2] * inv) | (f32_to_bf16(o[3] * inv) << 16);
+  *reinterpret_cast<uint2*>(dst) = r;
+}
+
+template <>
+__device__ __forceinline__ void store_out4<float>(void* dst, const float* o, float inv) {
+  *reinterpret_cast<float4*>(dst) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArgs a, int workers) {
-  using G = Geo<T, D>;
-  constexpr int LPT = G::kLpt, EPL = G::kEpl, ROW = G::kRowBytes;
+  constexpr int LPH = D / 4;                       // lanes per head
+  constexpr int HPW = merge_heads_per_wave<D>();   // heads per wave
   const int lane = threadIdx.x % 64;
-  const int col = lane % LPT;
   const int hps = a.heads_per_seg;
+  const int wpr = (hps + HPW - 1) / HPW;           // waves per record
   const int id = uniform((int)(blockIdx.x * kMergeWaves + threadIdx.x / 64));
-  const int w = id / hps;
-  const int g = id - w * hps;
+  const int w = id / wpr;
   if (w >= workers) return;
-  const MergeRecord r = a.records[w];
-  if (!r.valid) return;
-  const int64_t npieces = w - r.first + 1;
-  auto piece = [&](int64_t p) {   // partial record of piece p, head g
-    const int64_t ww = r.first + p;
-    const int64_t bw = ww * r.W / r.NW;
-    return a.partials + ((ww * 2 + (r.seg_start <= bw ? 0 : 1)) * a.group + g) * (D + 2);
-  };
-  // Running max over all pieces, then the rescaled sum.
-  float M = -INFINITY;
-  for (int64_t p0 = 0; p0 < npieces; p0 += 64) {
-    const float mp = p0 + lane < npieces ? piece(p0 + lane)[D] : -INFINITY;
-    M = fmaxf(M, mp);
-  }
+  typedef __attribute__((address_space(4))) const MergeRecord const_record;
+  const const_record* r = (const const_record*)a.records + w;   // scalar loads
+  if (!r->valid) return;
+  const int64_t first = r->first;
+  const int first_slot = r->first_slot;
+  const int g = (id - w * wpr) * HPW + lane / LPH;
+  if (g >= hps) return;   // no cross-lane work follows
+  const int d0 = (lane % LPH) * 4;
+  const int G = a.group;
+  const float* acc = a.partials;
+  const float2* pairs =
+      reinterpret_cast<const float2*>(a.partials + partial_pairs_offset(workers, G, D));
+  const int npieces = w - (int)first + 1;
+  float M = -INFINITY, S = 0.f;
+  float O[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < npieces; p0 += kMergeBatch) {
+    float4 ob[kMergeBatch];
+    float2 mb[kMergeBatch];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float S = 0.f;
-  for (int64_t p0 = 0; p0 < npieces; p0 += 64) {
-    if (p0 + lane < npieces) {
-      const float* P = piece(p0 + lane);
-      S += P[D + 1] * fast_exp2(P[D] - M);
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const int p = p0 + b;
+      if (p < npieces) {
+        const int64_t slot = ((first + p) * 2 + (p == 0 ? first_slot : 0)) * G + g;
+        mb[b] = pairs[slot];
+        ob[b] = *reinterpret_cast<const float4*>(acc + slot * D + d0);
+      } else {
+        mb[b] = make_float2(-INFINITY, 0.f);
+        ob[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
+    float Mb = M;
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) Mb = fmaxf(Mb, mb[b].x);
+    const float Mu = Mb == -INFINITY ? 0.f : Mb;
+    const float alpha = fast_exp2(M - Mu);
+    S *= alpha;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) O[e] *= alpha;
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const float f = fast_exp2(mb[b].x - Mu);
+      S = fmaf(mb[b].y, f, S);
+      O[0] = fmaf(ob[b].x, f, O[0]);
+      O[1] = fmaf(ob[b].y, f, O[1]);
+      O[2] = fmaf(ob[b].z, f, O[2]);
+      O[3] = fmaf(ob[b].w, f, O[3]);
+    }
+    M = Mb;
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
-  float O[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) O[e] = 0.f;
-  for (int64_t p = 0; p < npieces; ++p) {
-    const float* P = piece(p);
-    const float f = fast_exp2(P[D] - M);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) O[e] = fmaf(P[col * EPL + e], f, O[e]);
-  }
-  const int head = r.head * hps + g;
-  char* out_row = static_cast<char*>(a.out) + ((size_t)r.seq * a.num_q_heads + head) * ROW;
-  if (lane < LPT) store_out16<T>(out_row + col * 16, O, 1.f / S);
+  const int head = r->head * hps + g;
+  char* out_row =
+      static_cast<char*>(a.out) + ((size_t)r->seq * a.num_q_heads + head) * (D * sizeof(T));
+  store_out4<T>(out_row + d0 * sizeof(T), O, 1.f / S);
 }
 
 template <typename T, int D, int BS>
@@ -362,7 +399,8 @@ hipError_t launch_valu(const DecodeArgs* a, int workers, hipStream_t stream, int
 
 template <typename T, int D>
 hipError_t launch_merge(const DecodeArgs& a, int workers, hipStream_t stream) {
-  const int64_t waves = (int64_t)workers * a.heads_per_seg;
+  const int hpw = merge_heads_per_wave<D>();
+  const int64_t waves = (int64_t)workers * ((a.heads_per_seg + hpw - 1) / hpw);
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((waves + kMergeWaves - 1) / kMergeWaves)),
                      dim3(64 * kMergeWaves), 0, stream, a, workers);
   return hipGetLastError();

@@ -109,10 +109,10 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
     r.NW = ls.NW;
     r.seg_start = cur.seg_start;
     r.first = worker_of(cur.seg_start, ls.W, ls.NW);
+    r.first_slot = cur.seg_start > r.first * ls.W / ls.NW ? 1 : 0;
     r.seq = cur.s;
     r.head = cur.h;
     r.valid = (cur.seg_start < b0 && cur.seg_start + cur.n <= b1) ? 1 : 0;
-    r.pad = 0;
     a.records[w] = r;
   }
 
@@ -265,16 +265,17 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
           store_out16<uint16_t>(orow + i * 16, vals, inv);
         }
       } else {
-        const int which = mt.seg_start <= b0 ? 0 : 1;
-        float* P = a.partials + (((int64_t)w * 2 + which) * G + n) * (kD + 2);
+        const int64_t slot = ((int64_t)w * 2 + (mt.seg_start <= b0 ? 0 : 1)) * G + n;
+        float* acc = a.partials + slot * kD;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) P[g4 * 32 + i * 8 + k] = o[k][i];
+          for (int k = 0; k < 8; ++k) acc[g4 * 32 + i * 8 + k] = o[k][i];
         }
         if (g4 == 0) {
-          P[kD] = m;
-          P[kD + 1] = l;
+          float* pair = a.partials + partial_pairs_offset(nworkers, G, kD) + slot * 2;
+          pair[0] = m;
+          pair[1] = l;
         }
       }
     }

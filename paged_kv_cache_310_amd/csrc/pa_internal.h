@@ -27,7 +27,8 @@ struct MergeRecord {
   int64_t seg_start;  // first chunk of the segment
   int64_t first;      // worker holding that chunk
   int32_t seq, head;
-  int32_t valid, pad;
+  int32_t valid;
+  int32_t first_slot; // partial slot (0 or 1) the segment's piece has in worker `first`
 };
 
 static_assert(sizeof(MergeRecord) == 48, "merge record layout");
@@ -44,7 +45,7 @@ struct DecodeArgs {
   const void* v_new;
   const int64_t* slot_mapping;
   MergeRecord* records;       // [workers]
-  float* partials;            // [workers][2][group][head_dim + 2]
+  float* partials;            // acc [workers][2][group][head_dim], then (max, sum) [workers][2][group]
   int64_t max_blocks_per_seq;
   int num_seqs;
   int num_q_heads;
@@ -54,12 +55,19 @@ struct DecodeArgs {
   float scale_log2;           // scale * log2(e): scores live in the exp2 domain
 };
 
-// Workspace: one MergeRecord per worker, then per-worker partials, two
-// (max, sum, acc[head_dim]) records per worker and query head of a segment.
-// Everything is written before it is read in the same call, so the
-// workspace needs no initialisation.
+// Workspace: one MergeRecord per worker, then the partial pieces: two slots
+// per worker (the segment it continues, the segment it begins) and query head
+// of a segment, stored as all the unnormalised accumulators [workers][2]
+// [group][head_dim] followed by all the (max, sum) pairs [workers][2][group],
+// so that every accumulator row is 16-byte aligned.  Everything is written
+// before it is read in the same call, so the workspace needs no
+// initialisation.
 inline size_t records_bytes(int workers) {
   return ((size_t)workers * sizeof(MergeRecord) + 255) & ~(size_t)255;
+}
+// Offset, in floats from `partials`, of the (max, sum) pairs.
+__host__ __device__ inline int64_t partial_pairs_offset(int workers, int group, int head_dim) {
+  return (int64_t)workers * 2 * group * head_dim;
 }
 inline size_t partials_bytes(int workers, int group, int head_dim) {
   return records_bytes(workers) +
