@@ -89,7 +89,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
  * (0 = the library's default for the current device).  Writes *bytes.  The
  * workspace holds, per worker, a 48-byte merge record (the record array is
  * padded to 256 bytes) and partial results of the context split:
- * num_workers * 2 * (num_q_heads / num_kv_heads) * (head_dim + 2) floats.
+ * num_workers * 2 * (num_q_heads / num_kv_heads) * (head_dim + 4) floats.
  * It needs no initialisation; one workspace serves successive calls of any
  * shape in stream order (never two calls at once). */
 int pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

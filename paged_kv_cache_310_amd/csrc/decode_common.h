@@ -126,23 +126,28 @@ __device__ __forceinline__ void axpy16<float>(float* o, float p, const u32x4& v)
 }
 
 // Writes o * inv as one 16-byte piece of an output row.
+// Scales EPL accumulators by inv and packs them as 16 bytes of T.
 template <typename T>
-__device__ __forceinline__ void store_out16(void* dst, const float* o, float inv);
+__device__ __forceinline__ u32x4 pack16(const float* o, float inv);
 
 template <>
-__device__ __forceinline__ void store_out16<uint16_t>(void* dst, const float* o, float inv) {
-  uint4 r;
-  r.x = f32_to_bf16(o[0] * inv) | (f32_to_bf16(o[1] * inv) << 16);
-  r.y = f32_to_bf16(o[2] * inv) | (f32_to_bf16(o[3] * inv) << 16);
-  r.z = f32_to_bf16(o[4] * inv) | (f32_to_bf16(o[5] * inv) << 16);
-  r.w = f32_to_bf16(o[6] * inv) | (f32_to_bf16(o[7] * inv) << 16);
-  *reinterpret_cast<uint4*>(dst) = r;
+__device__ __forceinline__ u32x4 pack16<uint16_t>(const float* o, float inv) {
+  u32x4 r;
+  r[0] = f32_to_bf16(o[0] * inv) | (f32_to_bf16(o[1] * inv) << 16);
+  r[1] = f32_to_bf16(o[2] * inv) | (f32_to_bf16(o[3] * inv) << 16);
+  r[2] = f32_to_bf16(o[4] * inv) | (f32_to_bf16(o[5] * inv) << 16);
+  r[3] = f32_to_bf16(o[6] * inv) | (f32_to_bf16(o[7] * inv) << 16);
+  return r;
 }
 
 template <>
-__device__ __forceinline__ void store_out16<float>(void* dst, const float* o, float inv) {
-  float4 r = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-  *reinterpret_cast<float4*>(dst) = r;
+__device__ __forceinline__ u32x4 pack16<float>(const float* o, float inv) {
+  return u32x4{__float_as_uint(o[0] * inv), __float_as_uint(o[1] * inv),
+               __float_as_uint(o[2] * inv), __float_as_uint(o[3] * inv)};
+}
+
+__device__ __forceinline__ u32x4 f32x4_bits(float a, float b, float c, float d) {
+  return u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
 }
 
 __device__ __forceinline__ int chunks_of(int len) { return (len + kChunk - 1) / kChunk; }
@@ -243,16 +248,34 @@ __device__ __forceinline__ void locate_segment(const int32_t* lens, int num_seqs
 
 // Wave-uniform cursor over the chunk line: chunk c is chunk j (of n) of the
 // segment (head h, sequence s of length L) that starts at line chunk
-// seg_start.
+// seg_start.  slot is the sequence's fused-append slot (< 0: none), read
+// together with L so that a segment switch waits for one scalar load.
 struct Cursor {
   int64_t c;
   int64_t seg_start;
+  int64_t slot;
   int h, s, L, n, j;
 };
 
+__device__ __forceinline__ int64_t append_slot(const int64_t* slot_mapping, int s) {
+  return slot_mapping != nullptr ? ((const const_i64*)slot_mapping)[s] : -1;   // scalar load
+}
+
+// Places the cursor on chunk c (the first chunk of a worker's range).
+__device__ __forceinline__ void cursor_start(Cursor& k, const int32_t* lens, const int64_t* slots,
+                                             int num_seqs, int64_t wseq, int64_t c, int lane) {
+  k.c = c;
+  locate_segment(lens, num_seqs, wseq, c, lane, k.h, k.s, k.seg_start);
+  k.L = ((const const_i32*)lens)[k.s];
+  k.slot = append_slot(slots, k.s);
+  k.n = chunks_of(k.L);
+  k.j = (int)(c - k.seg_start);
+}
+
 // Moves the cursor to the next chunk of the line, skipping empty sequences.
 // Callers never move it past the last chunk of their range.
-__device__ __forceinline__ void cursor_next(Cursor& k, const int32_t* lens_ptr, int num_seqs) {
+__device__ __forceinline__ void cursor_next(Cursor& k, const int32_t* lens_ptr,
+                                            const int64_t* slots, int num_seqs) {
   const const_i32* lens = (const const_i32*)lens_ptr;   // scalar loads (lgkmcnt)
   ++k.c;
   if (++k.j < k.n) return;
@@ -262,6 +285,7 @@ __device__ __forceinline__ void cursor_next(Cursor& k, const int32_t* lens_ptr, 
       ++k.h;
     }
     k.L = lens[k.s];
+    k.slot = append_slot(slots, k.s);
   } while (k.L == 0);
   k.n = chunks_of(k.L);
   k.j = 0;
@@ -269,30 +293,131 @@ __device__ __forceinline__ void cursor_next(Cursor& k, const int32_t* lens_ptr, 
 }
 
 // What a tile carries about its chunk, so the consumer can switch segments
-// without draining the load pipeline.
-struct ChunkMeta {
-  int64_t seg_start;
-  int64_t slot;      // fused append into this segment's last chunk (< 0: none)
-  int h, s, L, n, j;
-  bool first;        // first chunk of the segment in this worker's range
-  bool last;         // last chunk of the segment in this worker's range
+// without draining the load pipeline.  Kept small: every tile in flight
+// holds one in scalar registers.
+enum ChunkFlags : int {
+  kFirst = 1,    // first chunk of the segment in this worker's range
+  kLast = 2,     // last chunk of the segment in this worker's range
+  kWhole = 4,    // the whole segment lies in this worker's range
+  kSecond = 8,   // the segment begins inside the range: partial slot 1
 };
 
-__device__ __forceinline__ ChunkMeta chunk_meta(const Cursor& k, int64_t b0, int64_t b1,
-                                               const int64_t* slot_mapping) {
+struct ChunkMeta {
+  int64_t slot;  // fused append into the segment, set on its last chunk (< 0: none)
+  int h, s;
+  int valid;     // cached tokens of the chunk to attend to (0..16)
+  int flags;
+  __device__ bool first() const { return flags & kFirst; }
+  __device__ bool last() const { return flags & kLast; }
+  __device__ bool whole() const { return flags & kWhole; }
+  __device__ int partial_slot() const { return (flags & kSecond) ? 1 : 0; }
+};
+
+__device__ __forceinline__ ChunkMeta chunk_meta(const Cursor& k, int64_t b0, int64_t b1) {
   ChunkMeta m;
-  m.seg_start = k.seg_start;
   m.h = k.h;
   m.s = k.s;
-  m.L = k.L;
-  m.n = k.n;
-  m.j = k.j;
-  m.first = k.c == b0 || k.j == 0;
-  m.last = k.c == b1 - 1 || k.j == k.n - 1;
-  m.slot = (slot_mapping != nullptr && k.j == k.n - 1)
-               ? ((const const_i64*)slot_mapping)[k.s]   // scalar load (lgkmcnt)
-               : -1;
+  const bool seg_last = k.j == k.n - 1;
+  m.flags = ((k.c == b0 || k.j == 0) ? kFirst : 0) | ((k.c == b1 - 1 || seg_last) ? kLast : 0) |
+            ((k.seg_start >= b0 && k.seg_start + k.n <= b1) ? kWhole : 0) |
+            (k.seg_start > b0 ? kSecond : 0);
+  m.slot = seg_last ? k.slot : -1;
+  // The appended token's pool slot is not written yet: it is attended to
+  // from k_new/v_new instead.
+  const int pool = k.L - (m.slot >= 0 ? 1 : 0) - k.j * kChunk;
+  m.valid = pool < kChunk ? pool : kChunk;
   return m;
+}
+
+// ---------------------------------------------------------------------------
+// Deferred stores.
+//
+// A wave's vector loads and stores complete through one in-order counter
+// (vmcnt).  A store issued between tile loads -- an output row at the end of
+// a segment -- makes the wait for every tile already in flight also wait for
+// the store's acknowledgement, about one memory latency per segment end when
+// the memory system is saturated.  Segment ends therefore write their rows to
+// a per-wave queue of 1 KiB slots in LDS, and every pipeline step drains
+// kQDrain slots with exactly kQDrain store instructions: a step with nothing
+// queued stores through a zero-length buffer range, which writes nothing.
+// Every step then issues the same loads and stores, and the compiler's waits
+// stay exact.  A job is `bytes` (a multiple of 16) contiguous bytes for one
+// destination; slot k of it covers bytes [1024k, 1024k + 1024).
+constexpr int kQSlots = 16;          // slots per wave (a power of two)
+constexpr int kQDrain = 1;           // slots drained per pipeline step
+
+struct QueueLds {
+  u32x4 data[kQSlots * 64];          // slot s, lane l: 16 bytes at 1024 s + 16 l
+  u32x4 meta[kQSlots];               // (dst low, dst high, bytes, 0)
+};
+
+typedef u32x4 __attribute__((address_space(3))) lds_u32x4;
+
+struct StoreQueue {
+  lds_u32x4* data;
+  lds_u32x4* meta;
+  int head, tail;                    // wave-uniform slot counters: [head, tail) queued
+};
+
+__device__ __forceinline__ StoreQueue queue_on(QueueLds& lds) {
+  StoreQueue q;
+  q.data = (lds_u32x4*)lds.data;
+  q.meta = (lds_u32x4*)lds.meta;
+  q.head = 0;
+  q.tail = 0;
+  return q;
+}
+
+// One store instruction: the slot at the head, or nothing when the queue is
+// empty (`any` is a valid device pointer used as the base of the empty range).
+__device__ __forceinline__ void queue_drain_one(StoreQueue& q, int lane, const void* any) {
+  // The counters are wave-uniform; reading them through readfirstlane lets
+  // the compiler build the store's buffer resource in scalar registers.
+  const int head = uniform(q.head);
+  const bool have = head < uniform(q.tail);
+  const int s = head & (kQSlots - 1);
+  const u32x4 mt = q.meta[s];
+  const u32x4 v = q.data[s * 64 + lane];
+  // readfirstlane yields a signed int: widen each half as unsigned.
+  const uint64_t dst = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(mt[1]) << 32) |
+                       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(mt[0]);
+  const int bytes = have ? __builtin_amdgcn_readfirstlane(mt[2]) : 0;
+  const __amdgpu_buffer_rsrc_t r =
+      tile_rsrc(have ? reinterpret_cast<const void*>(dst) : any, bytes);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, lane * 16, 0, 0);
+  q.head = head + (have ? 1 : 0);
+}
+
+// Reserves `n` (<= kQSlots) consecutive slots, storing synchronously while
+// the queue is too full; returns the first.  Wave-uniform control only.
+__device__ __forceinline__ int queue_reserve(StoreQueue& q, int n, int lane, const void* any) {
+  while (uniform(q.tail) + n - uniform(q.head) > kQSlots) queue_drain_one(q, lane, any);
+  const int first = uniform(q.tail);
+  q.tail = first + n;
+  return first;
+}
+
+__device__ __forceinline__ int queue_slots(int bytes) { return (bytes + 1023) >> 10; }
+
+// 16 bytes at byte offset `off` of the job whose first slot is `first`.
+__device__ __forceinline__ void queue_put(const StoreQueue& q, int first, int off, const u32x4& v) {
+  const int s = (first + (off >> 10)) & (kQSlots - 1);
+  q.data[s * 64 + ((off & 1023) >> 4)] = v;
+}
+
+// Destination of the job: `bytes` bytes at `dst`.  All lanes call it.
+__device__ __forceinline__ void queue_job(const StoreQueue& q, int first, const void* dst,
+                                          int bytes, int lane) {
+  if (lane < queue_slots(bytes)) {
+    const uint64_t d = reinterpret_cast<uint64_t>(dst) + (uint64_t)lane * 1024;
+    const int b = bytes - lane * 1024 < 1024 ? bytes - lane * 1024 : 1024;
+    q.meta[(first + lane) & (kQSlots - 1)] = u32x4{(uint32_t)d, (uint32_t)(d >> 32), (uint32_t)b, 0u};
+  }
+}
+
+// Stores everything still queued (end of the worker's range).
+__device__ __forceinline__ void queue_flush(StoreQueue& q, int lane, const void* any) {
+  while (uniform(q.head) < uniform(q.tail)) queue_drain_one(q, lane, any);
 }
 
 }  // namespace dev

@@ -47,12 +47,6 @@ namespace {
 
 using namespace dev;
 
-template <typename T, int D>
-struct Tile {
-  u32x4 k[Geo<T, D>::kNl];
-  u32x4 v[Geo<T, D>::kNl];
-};
-
 // Register budget: at least 2 waves per SIMD (256 VGPRs).  The default is
 // one worker per SIMD, so the budget goes to keeping two tiles, the segment's
 // q and the fused-append row in registers rather than to occupancy.
@@ -93,11 +87,7 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
   }
   const int64_t b0 = ls.b0, b1 = ls.b1;
   Cursor cur;
-  cur.c = b0;
-  locate_segment(lens, B, ls.wseq, b0, lane, cur.h, cur.s, cur.seg_start);
-  cur.L = lens[cur.s];
-  cur.n = chunks_of(cur.L);
-  cur.j = (int)(b0 - cur.seg_start);
+  cursor_start(cur, lens, a.slot_mapping, B, ls.wseq, b0, lane);
   if (lane == 0) {
     // This worker closes the split segment holding b0 if the segment began
     // in an earlier worker and ends inside this range.
@@ -127,11 +117,25 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     ChunkMeta meta;
   };
 
-  // Loads the chunk under the cursor, then moves the cursor (unless it is on
-  // the range's last chunk) and prefetches the next chunk's block number.
+  __shared__ QueueLds qlds;
+  StoreQueue q = queue_on(qlds);
+
+  // Loads the chunk under the cursor, drains kQDrain queued store slots, then
+  // moves the cursor (unless it is on the range's last chunk) and prefetches
+  // the next chunk's block number.  The conditional loads go first: if the
+  // compiler's in-order wait count assumes they were not issued, the extra
+  // wait falls on them, not on this tile's K/V loads.
   auto issue = [&](Tile& t) {
-    t.meta = chunk_meta(cur, b0, b1, a.slot_mapping);
+    t.meta = chunk_meta(cur, b0, b1);
     const int kvh = cur.h / a.group;
+    if (t.meta.slot >= 0) {
+      const size_t row = ((size_t)cur.s * HKV + kvh) * ROW;
+      t.kn = load16(tile_rsrc(static_cast<const char*>(a.k_new) + row, ROW), col * 16);
+      t.vn = load16(tile_rsrc(static_cast<const char*>(a.v_new) + row, ROW), col * 16);
+    }
+    if (t.meta.first())
+      t.q = load16(tile_rsrc(static_cast<const char*>(a.q) + ((size_t)cur.s * HQ + cur.h) * ROW,
+                             ROW), col * 16);
     const int64_t off = (int64_t)next_pb * block_stride + (int64_t)kvh * BS * ROW +
                         (int64_t)(cur.j % CPB) * kChunk * ROW;
     const __amdgpu_buffer_rsrc_t kr =
@@ -143,18 +147,12 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
       t.k[i] = load16(kr, i * 1024 + lane * 16);
       t.v[i] = load16(vr, i * 1024 + lane * 16);
     }
-    if (t.meta.first)
-      t.q = load16(tile_rsrc(static_cast<const char*>(a.q) + ((size_t)cur.s * HQ + cur.h) * ROW,
-                             ROW), col * 16);
-    if (t.meta.slot >= 0) {
-      const size_t row = ((size_t)cur.s * HKV + kvh) * ROW;
-      t.kn = load16(tile_rsrc(static_cast<const char*>(a.k_new) + row, ROW), col * 16);
-      t.vn = load16(tile_rsrc(static_cast<const char*>(a.v_new) + row, ROW), col * 16);
-    }
+#pragma unroll
+    for (int d = 0; d < kQDrain; ++d) queue_drain_one(q, lane, a.out);
     // Keep the loads ahead of the math on the other tile.
     __builtin_amdgcn_sched_barrier(0);
     if (cur.c + 1 < b1) {
-      cursor_next(cur, lens, B);
+      cursor_next(cur, lens, a.slot_mapping, B);
       next_pb = table_of(cur)[cur.j / CPB];
     }
   };
@@ -168,22 +166,21 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
 
   auto consume = [&](const Tile& t) {
     const ChunkMeta& mt = t.meta;
-    if (mt.first) {
+    if (mt.first()) {
       qv = t.q;
       m = -INFINITY;
       l = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = 0.f;
     }
-    // The newest token's pool slot is stale in a fused append: mask it here
-    // and add the token from k_new/v_new below.
-    const int L_pool = mt.slot >= 0 ? mt.L - 1 : mt.L;
-    const int tok0 = mt.j * kChunk + trow;
+    // Tokens past mt.valid (beyond the sequence, or the newest token whose
+    // pool slot is stale in a fused append: it is added from k_new/v_new
+    // below) are masked.
     float sc[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const float dot = row_sum<LPT>(dot16<T>(qv, t.k[i]));
-      sc[i] = tok0 + i * TPL < L_pool ? dot * a.scale_log2 : -INFINITY;
+      sc[i] = trow + i * TPL < mt.valid ? dot * a.scale_log2 : -INFINITY;
     }
     float mx = sc[0];
 #pragma unroll
@@ -198,17 +195,16 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     for (int i = 0; i < NL; ++i) {
       const float p = fast_exp2(sc[i] - m_use);
       l += p;
-      const u32x4 vv = tok0 + i * TPL < L_pool ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 vv = trow + i * TPL < mt.valid ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
       axpy16<T>(o, p, vv);
     }
     m = m_new;
-    if (!mt.last) return;
+    if (!mt.last()) return;
 
     // ---- end of this worker's part of the segment
     const int kvh = mt.h / a.group;
     if (mt.slot >= 0) {
-      // The newest token joins token row 0; its K/V row goes to its slot
-      // (written once per KV head, by the group's first query head).
+      // The newest token joins token row 0.
       const float dot = row_sum<LPT>(dot16<T>(qv, t.kn));
       if (trow == 0) {
         const float s_new = dot * a.scale_log2;
@@ -220,13 +216,20 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
         for (int e = 0; e < EPL; ++e) o[e] *= al;
         axpy16<T>(o, p, t.vn);
         m = mm;
-        if (mt.h % a.group == 0) {
-          const int64_t blk = mt.slot / BS;
-          const int64_t pos = mt.slot - blk * BS;
-          const int64_t row_off = ((blk * HKV + kvh) * BS + pos) * ROW + col * 16;
-          *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) + row_off) = t.kn;
-          *reinterpret_cast<u32x4*>(static_cast<char*>(a.v_cache) + row_off) = t.vn;
+      }
+      if (mt.h % a.group == 0) {
+        // Its K/V rows go to its pool slot, once per KV head (by the
+        // group's first query head).
+        const int64_t blk = mt.slot / BS;
+        const int64_t pos = mt.slot - blk * BS;
+        const int64_t row_off = ((blk * HKV + kvh) * BS + pos) * ROW;
+        const int f = queue_reserve(q, 2, lane, a.out);
+        if (lane < LPT) {
+          queue_put(q, f, col * 16, t.kn);
+          queue_put(q, f + 1, col * 16, t.vn);
         }
+        queue_job(q, f, static_cast<char*>(a.k_cache) + row_off, ROW, lane);
+        queue_job(q, f + 1, static_cast<char*>(a.v_cache) + row_off, ROW, lane);
       }
     }
     // Merge the token rows of the wavefront (lanes with equal col).
@@ -246,47 +249,41 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
       }
       m = mm;
     }
-    const bool whole = mt.seg_start >= b0 && mt.seg_start + mt.n <= b1;
-    if (whole) {
-      char* out_row = static_cast<char*>(a.out) + ((size_t)mt.s * HQ + mt.h) * ROW;
-      if (lane < LPT) store_out16<T>(out_row + col * 16, o, 1.f / l);
+    const int f = queue_reserve(q, 1, lane, a.out);
+    if (mt.whole()) {
+      if (lane < LPT) queue_put(q, f, col * 16, pack16<T>(o, 1.f / l));
+      queue_job(q, f, static_cast<char*>(a.out) + ((size_t)mt.s * HQ + mt.h) * ROW, ROW, lane);
     } else {
-      // Partial piece: publish (max, sum, acc); the merge kernel combines
+      // Partial piece: (acc, max, sum) for the merge kernel, which combines
       // the pieces after this launch.
-      const int64_t slot = ((int64_t)w * 2 + (mt.seg_start <= b0 ? 0 : 1)) * a.group;
+      constexpr int REC = D + kPartialExtra;
       if (lane < LPT) {
-        float* acc = a.partials + slot * D + col * EPL;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = o[e];
+        for (int u = 0; u < EPL / 4; ++u)
+          queue_put(q, f, (col * EPL + 4 * u) * 4,
+                    f32x4_bits(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]));
       }
-      if (lane == 0) {
-        float* pair = a.partials + partial_pairs_offset(nworkers, a.group, D) + slot * 2;
-        pair[0] = m;
-        pair[1] = l;
-      }
+      if (lane == 0) queue_put(q, f, D * 4, f32x4_bits(m, l, 0.f, 0.f));
+      queue_job(q, f, a.partials + ((int64_t)w * 2 + mt.partial_slot()) * a.group * REC, REC * 4,
+                lane);
     }
   };
 
-  // Two tiles in ping-pong over the whole range: the steady-state loop issues
-  // unconditionally, so every path into a consume has the same tile loads in
-  // flight, and segment switches never drain the pipeline.
+  // Two tiles in ping-pong over the whole range.  Every issue is
+  // unconditional -- past the range's end the cursor stays on its last chunk,
+  // and such issues are never consumed -- so every consume sees the same
+  // loads in flight and segment switches never drain the pipeline.
   const int64_t count = b1 - b0;
-  Tile ta, tb;
-  issue(ta);
-  int64_t i = 0;
-  for (; i + 2 < count; i += 2) {
-    issue(tb);
-    consume(ta);
-    issue(ta);
-    consume(tb);
+  Tile t[2];
+  issue(t[0]);
+  for (int64_t i = 0; i < count; i += 2) {
+    issue(t[1]);
+    consume(t[0]);
+    if (i + 1 >= count) break;
+    issue(t[0]);
+    consume(t[1]);
   }
-  if (i + 1 < count) {
-    issue(tb);
-    consume(ta);
-    consume(tb);
-  } else {
-    consume(ta);
-  }
+  queue_flush(q, lane, a.out);
 }
 
 // Merges the partial pieces of every segment that spans several workers.
@@ -340,9 +337,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   if (g >= hps) return;   // no cross-lane work follows
   const int d0 = (lane % LPH) * 4;
   const int G = a.group;
-  const float* acc = a.partials;
-  const float2* pairs =
-      reinterpret_cast<const float2*>(a.partials + partial_pairs_offset(workers, G, D));
+  constexpr int REC = D + kPartialExtra;   // acc[D], max, sum, pad
   const int npieces = w - (int)first + 1;
   float M = -INFINITY, S = 0.f;
   float O[4] = {0.f, 0.f, 0.f, 0.f};
@@ -354,8 +349,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
       const int p = p0 + b;
       if (p < npieces) {
         const int64_t slot = ((first + p) * 2 + (p == 0 ? first_slot : 0)) * G + g;
-        mb[b] = pairs[slot];
-        ob[b] = *reinterpret_cast<const float4*>(acc + slot * D + d0);
+        const float* rec = a.partials + slot * REC;
+        mb[b] = *reinterpret_cast<const float2*>(rec + D);
+        ob[b] = *reinterpret_cast<const float4*>(rec + d0);
       } else {
         mb[b] = make_float2(-INFINITY, 0.f);
         ob[b] = make_float4(0.f, 0.f, 0.f, 0.f);

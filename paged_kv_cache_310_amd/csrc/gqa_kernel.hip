@@ -67,8 +67,12 @@ __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
   return (e & 1) ? bf_hi(d) : bf_lo(d);
 }
 
+// Tiles per wave: one consumed while the others are in flight.  A third
+// tile measured no faster.
+constexpr int kRing = 2;
+
 template <int BS>
-__global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
   constexpr int CPB = BS / kChunk;
   static_assert(BS % kChunk == 0, "block size must be a multiple of the chunk");
   const int lane = threadIdx.x;
@@ -98,11 +102,7 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
   }
   const int64_t b0 = ls.b0, b1 = ls.b1;
   Cursor cur;
-  cur.c = b0;
-  locate_segment(lens, B, ls.wseq, b0, lane, cur.h, cur.s, cur.seg_start);
-  cur.L = lens[cur.s];
-  cur.n = chunks_of(cur.L);
-  cur.j = (int)(b0 - cur.seg_start);
+  cursor_start(cur, lens, a.slot_mapping, B, ls.wseq, b0, lane);
   if (lane == 0) {
     MergeRecord r;
     r.W = ls.W;
@@ -119,6 +119,8 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
   const int64_t block_stride = (int64_t)HKV * BS * kRow;
   const bool real_head = n < G;
   const int krow_off = token_of(n) * kRow + g4 * 16;
+  // Padding heads (n >= G) read past the group's rows: the buffer returns 0.
+  const int qoff = n * kRow + g4 * 16;
   auto table_of = [&](const Cursor& k) {
     return (const const_i32*)(a.block_tables + (int64_t)k.s * a.max_blocks_per_seq);
   };
@@ -127,60 +129,78 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
   struct Tile {
     u32x4 k[4];            // K operand: token token_of(l%16), dims 32c + 8(l/16)
     u32x4 v[4];            // V rows: load i = token 4i + l/16, dims 8(l%16)..+8
-    u32x4 q[4];            // Q^T operand of the segment, valid when meta.first
+    u32x4 q[4];            // Q^T operand: head l%16, dims 32c + 8(l/16)
+    u32x4 kn[4], vn[4];    // newest token (fused append), valid when meta.slot >= 0
     ChunkMeta meta;
   };
 
+  __shared__ QueueLds qlds;
+  StoreQueue q = queue_on(qlds);
+
+  // Every tile issues the same tile loads and queue stores (a fixed count
+  // keeps the compiler's in-order wait counts exact).  Rows past the chunk's
+  // valid tokens lie outside the tile's buffer range and read as 0.  The
+  // newest token's rows, loaded only with a segment's last chunk, go first:
+  // a wait count that assumes they were not issued then waits for them, not
+  // for this tile.  Past the end of the range the cursor stays on the last
+  // chunk: such issues reload it and are never consumed.
   auto issue = [&](Tile& t) {
-    t.meta = chunk_meta(cur, b0, b1, a.slot_mapping);
+    t.meta = chunk_meta(cur, b0, b1);
+    if (t.meta.slot >= 0) {
+      const size_t row = ((size_t)cur.s * HKV + cur.h) * kRow;
+      const __amdgpu_buffer_rsrc_t knr = tile_rsrc(static_cast<const char*>(a.k_new) + row, kRow);
+      const __amdgpu_buffer_rsrc_t vnr = tile_rsrc(static_cast<const char*>(a.v_new) + row, kRow);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t.kn[k] = load16(knr, k * 64 + g4 * 16);   // dims 32k + 8*g4
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t.vn[i] = load16(vnr, g4 * 64 + i * 16);   // dims 32*g4 + 8i
+    }
     const int64_t off = (int64_t)next_pb * block_stride + (int64_t)cur.h * BS * kRow +
                         (int64_t)(cur.j % CPB) * kTile;
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(static_cast<const char*>(a.k_cache) + off, kTile);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(static_cast<const char*>(a.v_cache) + off, kTile);
+    const int bytes = uniform((t.meta.valid > 0 ? t.meta.valid : 0) * kRow);
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(static_cast<const char*>(a.k_cache) + off, bytes);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(static_cast<const char*>(a.v_cache) + off, bytes);
+    const __amdgpu_buffer_rsrc_t qr = tile_rsrc(
+        static_cast<const char*>(a.q) + ((size_t)cur.s * HQ + cur.h * G) * kRow, G * kRow);
 #pragma unroll
     for (int k = 0; k < 4; ++k) t.k[k] = load16(kr, krow_off + k * 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) t.v[i] = load16(vr, i * 1024 + lane * 16);
-    if (t.meta.first) {
-      // head n of the group, dims 32k + 8*g4 .. +8 (padding heads read head 0, zeroed later)
-      const __amdgpu_buffer_rsrc_t qr = tile_rsrc(
-          static_cast<const char*>(a.q) + ((size_t)cur.s * HQ + cur.h * G) * kRow, G * kRow);
-      const int qoff = (real_head ? n : 0) * kRow + g4 * 16;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) t.q[k] = load16(qr, qoff + k * 64);
-    }
+    for (int k = 0; k < 4; ++k) t.q[k] = load16(qr, qoff + k * 64);
+#pragma unroll
+    for (int d = 0; d < kQDrain; ++d) queue_drain_one(q, lane, a.out);
     __builtin_amdgcn_sched_barrier(0);
     if (cur.c + 1 < b1) {
-      cursor_next(cur, lens, B);
+      cursor_next(cur, lens, a.slot_mapping, B);
       next_pb = table_of(cur)[cur.j / CPB];
     }
   };
 
-  u32x4 qf[4];
   float m = -INFINITY, l = 0.f;
   f32x4_t o[8];
 
   auto consume = [&](const Tile& t) {
     const ChunkMeta& mt = t.meta;
-    if (mt.first) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qf[k] = real_head ? t.q[k] : u32x4{0u, 0u, 0u, 0u};
+    if (mt.first()) {
       m = -INFINITY;
       l = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const int L_pool = mt.slot >= 0 ? mt.L - 1 : mt.L;
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[k]),
-                                                      __builtin_bit_cast(bf16x8_t, qf[k]),
+                                                      __builtin_bit_cast(bf16x8_t, t.q[k]),
                                                       sacc, 0, 0, 0);
-    const int base = mt.j * kChunk + g4;   // lane holds tokens base + 4i
     float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = base + 4 * i < L_pool ? sacc[i] * a.scale_log2 : -INFINITY;
+    for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * a.scale_log2;
+    if (mt.valid < kChunk) {   // the segment's last chunk: lane holds tokens g4 + 4i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = g4 + 4 * i < mt.valid ? sc[i] : -INFINITY;
+    }
     const float mx = group4_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     const float m_new = fmaxf(m, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -199,35 +219,23 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
       l += (float)pb[i];
     }
     const i16x4_t pop = __builtin_bit_cast(i16x4_t, pb);
-    u32x4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = base + 4 * i < L_pool ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
       const int dw = k >> 1;
-      const uint32_t lo = __builtin_amdgcn_perm(v[1][dw], v[0][dw], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(v[3][dw], v[2][dw], sel);
+      const uint32_t lo = __builtin_amdgcn_perm(t.v[1][dw], t.v[0][dw], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(t.v[3][dw], t.v[2][dw], sel);
       const i16x4_t va = __builtin_bit_cast(i16x4_t, (uint64_t)lo | ((uint64_t)hi << 32));
       o[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pop, o[k], 0, 0, 0);
     }
-    if (!mt.last) return;
+    if (!mt.last()) return;
 
     // ---- end of this worker's part of the segment
     l = group4_sum(l);   // every lane of head n now holds the head's full sum
     if (mt.slot >= 0) {
-      // The newest token's rows, read here (once per appended segment).
-      const size_t row = ((size_t)mt.s * HKV + mt.h) * kRow;
-      const __amdgpu_buffer_rsrc_t knr = tile_rsrc(static_cast<const char*>(a.k_new) + row, kRow);
-      const __amdgpu_buffer_rsrc_t vnr = tile_rsrc(static_cast<const char*>(a.v_new) + row, kRow);
-      u32x4 kn[4], vn[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) kn[k] = load16(knr, k * 64 + g4 * 16);   // dims 32k + 8*g4
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vn[i] = load16(vnr, g4 * 64 + i * 16);   // dims 32*g4 + 8i
       float d = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d = dot16<uint16_t>(qf[k], kn[k]) + d;
+      for (int k = 0; k < 4; ++k) d = dot16<uint16_t>(t.q[k], t.kn[k]) + d;
       const float s_new = group4_sum(d) * a.scale_log2;
       const float mm = fmaxf(m, s_new);
       const float al = fast_exp2(m - mm);
@@ -236,68 +244,75 @@ __global__ __launch_bounds__(64, 2) void decode_gqa_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k][i] = fmaf(p, bf16_elem(vn[i], k), o[k][i] * al);
+        for (int k = 0; k < 8; ++k) o[k][i] = fmaf(p, bf16_elem(t.vn[i], k), o[k][i] * al);
       }
       m = mm;
+      // Its K/V rows go to its pool slot: lanes 0, 16, 32, 48 hold every
+      // 16-byte piece of both.
+      const int64_t blk = mt.slot / BS;
+      const int64_t pos = mt.slot - blk * BS;
+      const int64_t row_off = ((blk * HKV + mt.h) * BS + pos) * kRow;
+      const int f = queue_reserve(q, 2, lane, a.out);
       if (n == 0) {
-        // lanes 0, 16, 32, 48 hold every 16-byte piece of both rows
-        const int64_t blk = mt.slot / BS;
-        const int64_t pos = mt.slot - blk * BS;
-        char* krow = static_cast<char*>(a.k_cache) + ((blk * HKV + mt.h) * BS + pos) * kRow;
-        char* vrow = static_cast<char*>(a.v_cache) + ((blk * HKV + mt.h) * BS + pos) * kRow;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          *reinterpret_cast<u32x4*>(krow + k * 64 + g4 * 16) = kn[k];
-          *reinterpret_cast<u32x4*>(vrow + g4 * 64 + k * 16) = vn[k];
+          queue_put(q, f, k * 64 + g4 * 16, t.kn[k]);
+          queue_put(q, f + 1, g4 * 64 + k * 16, t.vn[k]);
         }
       }
+      queue_job(q, f, static_cast<char*>(a.k_cache) + row_off, kRow, lane);
+      queue_job(q, f + 1, static_cast<char*>(a.v_cache) + row_off, kRow, lane);
     }
-    if (real_head) {
-      const bool whole = mt.seg_start >= b0 && mt.seg_start + mt.n <= b1;
-      if (whole) {
-        char* orow = static_cast<char*>(a.out) + ((size_t)mt.s * HQ + mt.h * G + n) * kRow + g4 * 64;
+    if (mt.whole()) {
+      // Output rows of the group's heads: G x 256 contiguous bytes.
+      const int bytes = G * kRow;
+      const int f = queue_reserve(q, queue_slots(bytes), lane, a.out);
+      if (real_head) {
         const float inv = 1.f / l;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float vals[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) vals[k] = o[k][i];
-          store_out16<uint16_t>(orow + i * 16, vals, inv);
-        }
-      } else {
-        const int64_t slot = ((int64_t)w * 2 + (mt.seg_start <= b0 ? 0 : 1)) * G + n;
-        float* acc = a.partials + slot * kD;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) acc[g4 * 32 + i * 8 + k] = o[k][i];
-        }
-        if (g4 == 0) {
-          float* pair = a.partials + partial_pairs_offset(nworkers, G, kD) + slot * 2;
-          pair[0] = m;
-          pair[1] = l;
+          queue_put(q, f, n * kRow + g4 * 64 + i * 16, pack16<uint16_t>(vals, inv));
         }
       }
+      queue_job(q, f, static_cast<char*>(a.out) + ((size_t)mt.s * HQ + mt.h * G) * kRow, bytes,
+                lane);
+    } else {
+      // Partial pieces (acc, max, sum) of the group's heads for the merge
+      // kernel: lane (n, g4) holds dims 32 g4 + 8i + k as o[k][i].
+      constexpr int REC = kD + kPartialExtra;
+      const int bytes = G * REC * 4;
+      const int f = queue_reserve(q, queue_slots(bytes), lane, a.out);
+      if (real_head) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int off = (n * REC + g4 * 32 + i * 8) * 4;
+          queue_put(q, f, off, f32x4_bits(o[0][i], o[1][i], o[2][i], o[3][i]));
+          queue_put(q, f, off + 16, f32x4_bits(o[4][i], o[5][i], o[6][i], o[7][i]));
+        }
+        if (g4 == 0) queue_put(q, f, (n * REC + kD) * 4, f32x4_bits(m, l, 0.f, 0.f));
+      }
+      queue_job(q, f, a.partials + ((int64_t)w * 2 + mt.partial_slot()) * G * REC, bytes, lane);
     }
   };
 
+  // Ring of kRing tiles: kRing - 1 in flight while one is consumed.  All
+  // issues are unconditional, so every consume sees the same loads in flight.
   const int64_t count = b1 - b0;
-  Tile ta, tb;
-  issue(ta);
-  int64_t i = 0;
-  for (; i + 2 < count; i += 2) {
-    issue(tb);
-    consume(ta);
-    issue(ta);
-    consume(tb);
+  Tile t[kRing];
+#pragma unroll
+  for (int r = 0; r + 1 < kRing; ++r) issue(t[r]);
+  for (int64_t i = 0; i < count; i += kRing) {
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      if (r > 0 && i + r >= count) break;
+      issue(t[(r + kRing - 1) % kRing]);
+      consume(t[r]);
+    }
   }
-  if (i + 1 < count) {
-    issue(tb);
-    consume(ta);
-    consume(tb);
-  } else {
-    consume(ta);
-  }
+  queue_flush(q, lane, a.out);
 }
 
 }  // namespace

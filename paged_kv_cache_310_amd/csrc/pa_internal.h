@@ -45,7 +45,7 @@ struct DecodeArgs {
   const void* v_new;
   const int64_t* slot_mapping;
   MergeRecord* records;       // [workers]
-  float* partials;            // acc [workers][2][group][head_dim], then (max, sum) [workers][2][group]
+  float* partials;            // [workers][2][group][head_dim + 4]: acc, max, sum, pad
   int64_t max_blocks_per_seq;
   int num_seqs;
   int num_q_heads;
@@ -57,21 +57,18 @@ struct DecodeArgs {
 
 // Workspace: one MergeRecord per worker, then the partial pieces: two slots
 // per worker (the segment it continues, the segment it begins) and query head
-// of a segment, stored as all the unnormalised accumulators [workers][2]
-// [group][head_dim] followed by all the (max, sum) pairs [workers][2][group],
-// so that every accumulator row is 16-byte aligned.  Everything is written
-// before it is read in the same call, so the workspace needs no
-// initialisation.
+// of a segment, each a record of head_dim + 4 floats: the unnormalised
+// accumulator, the running max, the sum and two floats of padding (records
+// stay 16-byte aligned).  Everything is written before it is read in the same
+// call, so the workspace needs no initialisation.
+constexpr int kPartialExtra = 4;
+__host__ __device__ inline int partial_floats(int head_dim) { return head_dim + kPartialExtra; }
 inline size_t records_bytes(int workers) {
   return ((size_t)workers * sizeof(MergeRecord) + 255) & ~(size_t)255;
 }
-// Offset, in floats from `partials`, of the (max, sum) pairs.
-__host__ __device__ inline int64_t partial_pairs_offset(int workers, int group, int head_dim) {
-  return (int64_t)workers * 2 * group * head_dim;
-}
 inline size_t partials_bytes(int workers, int group, int head_dim) {
   return records_bytes(workers) +
-         (size_t)workers * 2 * (size_t)group * (size_t)(head_dim + 2) * sizeof(float);
+         (size_t)workers * 2 * (size_t)group * (size_t)partial_floats(head_dim) * sizeof(float);
 }
 
 // Launches the attention kernel (recording `before`/`after`, when not null,

@@ -54,9 +54,9 @@ def test_workspace_size_formula(lib):
     sz = ctypes.c_size_t(0)
     rec = lambda w: (w * 48 + 255) // 256 * 256     # one 48-byte merge record per worker
     assert lib.pa_decode_workspace_size(32, 40, 40, 128, 4096, ctypes.byref(sz)) == 0
-    assert sz.value == rec(4096) + 4096 * 2 * 1 * 130 * 4
+    assert sz.value == rec(4096) + 4096 * 2 * 1 * 132 * 4
     assert lib.pa_decode_workspace_size(256, 64, 8, 128, 100, ctypes.byref(sz)) == 0
-    assert sz.value == rec(100) + 100 * 2 * 8 * 130 * 4
+    assert sz.value == rec(100) + 100 * 2 * 8 * 132 * 4
     assert lib.pa_decode_workspace_size(4, 6, 4, 64, 8, ctypes.byref(sz)) == 1   # 6 % 4 != 0
 
 
