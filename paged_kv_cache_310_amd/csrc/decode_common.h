@@ -19,6 +19,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef const int32_t __attribute__((address_space(4))) const_i32;
 typedef const int64_t __attribute__((address_space(4))) const_i64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t __attribute__((address_space(3))) lds_i32;
 
 // Buffer resource for one tile: scalar 48-bit base, byte range [0, bytes).
 // Loads through it take a 32-bit per-lane offset and return 0 outside the range.
@@ -176,74 +177,134 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t x, int lane) {
   return x;
 }
 
-// Worker that owns chunk c of the line [0, W) split over nw workers.
-__device__ __forceinline__ int64_t worker_of(int64_t c, int64_t W, int64_t nw) {
-  return ((c + 1) * nw + W - 1) / W - 1;
-}
+// ---------------------------------------------------------------------------
+// Work split.
+//
+// The chunk line holds all (head, sequence, 16-token chunk) triples,
+// head-major.  Workers get equal shares of work units rather than of chunks:
+// a segment costs its chunks plus seg_cost units for what each segment adds
+// besides its chunks (the end of the segment, where its output or partial is
+// produced, and the switch to the next one), so a worker whose range crosses
+// many short segments gets fewer chunks.  A segment's units are its seg_cost
+// overhead units followed by one unit per chunk; a worker owns the chunks
+// whose units fall in its unit range.  With seg_cost = 0 the split is an
+// equal split of chunks.
+constexpr int kLenCache = 4096;   // sequences whose chunk counts are cached in LDS
 
-// Finds the sequence holding chunk offset r (0 <= r < sum of chunks) and the
-// number of chunks before it.
-__device__ void locate_sequence(const int32_t* lens, int num_seqs, int64_t r, int lane,
-                                int& seq, int64_t& before) {
-  int64_t acc = 0;
-  for (int base = 0; base < num_seqs; base += 64) {
-    const int s = base + lane;
-    const int64_t n = s < num_seqs ? chunks_of(lens[s]) : 0;
-    const int64_t incl = wave_inclusive_scan(n, lane);
-    const int64_t total = uniform((int64_t)__shfl(incl, 63));
-    if (r < acc + total) {
-      const unsigned long long hit = __ballot(acc + incl > r);
-      const int first = __ffsll((long long)hit) - 1;
-      seq = uniform(base + first);
-      before = uniform((int64_t)(acc + __shfl(incl - n, first)));
-      return;
-    }
-    acc += total;
-  }
-  seq = num_seqs - 1;   // unreachable for r inside the line
-  before = acc;
-}
-
-// The chunk line: all (head, sequence, 16-token chunk) triples, head-major,
-// split into equal contiguous ranges [b0, b1) over the workers.
-struct LineSplit {
-  int64_t wseq;   // chunks per head: sum over sequences of ceil(L / 16)
-  int64_t W;      // chunks in the line
-  int64_t NW;     // workers with a non-empty range: min(workers, W)
-  int64_t b0, b1;
+struct SplitLds {
+  int32_t n[kLenCache];           // chunks of sequence s
 };
 
-// Computes the split for worker w; false when w has no chunks.
-__device__ __forceinline__ bool split_line(const int32_t* lens, int num_seqs, int num_heads,
-                                           int nworkers, int w, int lane, LineSplit& ls) {
-  int64_t wseq = 0;
-  for (int base = 0; base < num_seqs; base += 256) {
-    int64_t n = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = base + k * 64 + lane;
-      if (s < num_seqs) n += chunks_of(lens[s]);
-    }
-    wseq += uniform(wave_sum(n));
-  }
-  ls.wseq = wseq;
-  ls.W = wseq * num_heads;
-  if (ls.W == 0) return false;
-  ls.NW = ls.W < nworkers ? ls.W : nworkers;
-  if (w >= ls.NW) return false;
-  ls.b0 = (int64_t)w * ls.W / ls.NW;
-  ls.b1 = (int64_t)(w + 1) * ls.W / ls.NW;
-  return true;
+struct LineSplit {
+  int64_t wseq, useq;   // chunks / units per head
+  int64_t W, U;         // chunks / units in the line
+  int64_t NW;           // workers with a non-empty unit range: min(workers, U)
+  int64_t u0, u1;       // this worker's units
+  int64_t b0, b1;       // its chunks [b0, b1)
+  int h, s;             // segment holding b0
+  int64_t seg_start;    // its first chunk
+  int64_t seg_unit;     // its first unit
+};
+
+__device__ __forceinline__ int seq_chunks(const SplitLds& C, const int32_t* lens, int s) {
+  return s < kLenCache ? ((const lds_i32*)C.n)[s] : chunks_of(lens[s]);
 }
 
-// The segment (head h, sequence s) holding chunk c, and where it starts.
-__device__ __forceinline__ void locate_segment(const int32_t* lens, int num_seqs, int64_t wseq,
-                                               int64_t c, int lane, int& h, int& s,
-                                               int64_t& seg_start) {
-  h = (int)(c / wseq);
-  int64_t before = 0;
-  locate_sequence(lens, num_seqs, c - (int64_t)h * wseq, lane, s, before);
-  seg_start = (int64_t)h * wseq + before;
+// Worker that owns unit u of the line [0, U) split over nw workers.
+__device__ __forceinline__ int64_t worker_of(int64_t u, int64_t U, int64_t nw) {
+  return ((u + 1) * nw + U - 1) / U - 1;
+}
+
+// The first chunk whose unit is >= u (W if none), and its segment.
+__device__ void locate_unit(const SplitLds& C, const int32_t* lens, int num_seqs, int seg_cost,
+                            const LineSplit& ls, int64_t u, int lane, int64_t& c, int& h, int& s,
+                            int64_t& seg_start, int64_t& seg_unit) {
+  c = ls.W;
+  h = 0;
+  s = 0;
+  seg_start = ls.W;
+  seg_unit = ls.U;
+  if (u >= ls.U) return;
+  h = (int)(u / ls.useq);
+  const int64_t r = u - (int64_t)h * ls.useq;
+  int64_t acc_u = 0, acc_c = 0;
+  for (int base = 0; base < num_seqs; base += 64) {
+    const int sq = base + lane;
+    const int64_t n = sq < num_seqs ? seq_chunks(C, lens, sq) : 0;
+    const int64_t un = n > 0 ? n + seg_cost : 0;
+    const int64_t incl_u = wave_inclusive_scan(un, lane);
+    const int64_t incl_c = wave_inclusive_scan(n, lane);
+    const int64_t tot_u = uniform((int64_t)__shfl(incl_u, 63));
+    if (r < acc_u + tot_u) {
+      const unsigned long long hit = __ballot(acc_u + incl_u > r);
+      const int first = __ffsll((long long)hit) - 1;
+      s = uniform(base + first);
+      const int64_t bu = uniform((int64_t)(acc_u + __shfl(incl_u - un, first)));
+      const int64_t bc = uniform((int64_t)(acc_c + __shfl(incl_c - n, first)));
+      const int64_t off = r - bu;
+      seg_start = (int64_t)h * ls.wseq + bc;
+      seg_unit = (int64_t)h * ls.useq + bu;
+      c = seg_start + (off < seg_cost ? 0 : off - seg_cost);
+      return;
+    }
+    acc_u += tot_u;
+    acc_c += uniform((int64_t)__shfl(incl_c, 63));
+  }
+}
+
+// Computes the split for worker w; false when w has no chunks.  Caches the
+// sequences' chunk counts in C on the way.
+__device__ __forceinline__ bool split_line(SplitLds& C, const int32_t* lens, int num_seqs,
+                                           int num_heads, int seg_cost, int nworkers, int w,
+                                           int lane, LineSplit& ls) {
+  int64_t wseq = 0, useq = 0;
+  for (int base = 0; base < num_seqs; base += 256) {
+    int64_t n = 0, un = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sq = base + k * 64 + lane;
+      if (sq < num_seqs) {
+        const int c = chunks_of(lens[sq]);
+        if (sq < kLenCache) ((lds_i32*)C.n)[sq] = c;
+        n += c;
+        un += c > 0 ? c + seg_cost : 0;
+      }
+    }
+    wseq += uniform(wave_sum(n));
+    useq += uniform(wave_sum(un));
+  }
+  ls.wseq = wseq;
+  ls.useq = useq;
+  ls.W = wseq * num_heads;
+  ls.U = useq * num_heads;
+  if (ls.U == 0) return false;
+  ls.NW = ls.U < nworkers ? ls.U : nworkers;
+  if (w >= ls.NW) return false;
+  ls.u0 = (int64_t)w * ls.U / ls.NW;
+  ls.u1 = (int64_t)(w + 1) * ls.U / ls.NW;
+  int h1, s1;
+  int64_t st1, su1;
+  locate_unit(C, lens, num_seqs, seg_cost, ls, ls.u0, lane, ls.b0, ls.h, ls.s, ls.seg_start,
+              ls.seg_unit);
+  locate_unit(C, lens, num_seqs, seg_cost, ls, ls.u1, lane, ls.b1, h1, s1, st1, su1);
+  return ls.b0 < ls.b1;
+}
+
+// What the merge kernel needs about the segment holding b0: worker `first`
+// holds its first chunk, and the partial slot of the segment's piece there.
+__device__ __forceinline__ MergeRecord merge_record(const LineSplit& ls, int seg_cost, int n) {
+  MergeRecord r;
+  r.W = ls.U;
+  r.NW = ls.NW;
+  r.seg_start = ls.seg_start;
+  r.first = worker_of(ls.seg_unit + seg_cost, ls.U, ls.NW);
+  // Slot 1 when worker `first` has chunks (of earlier segments) before this
+  // segment: its unit range starts before the segment's first unit.
+  r.first_slot = r.first * ls.U / ls.NW < ls.seg_unit ? 1 : 0;
+  r.seq = ls.s;
+  r.head = ls.h;
+  r.valid = (ls.seg_start < ls.b0 && ls.seg_start + n <= ls.b1) ? 1 : 0;
+  return r;
 }
 
 // Wave-uniform cursor over the chunk line: chunk c is chunk j (of n) of the
@@ -261,15 +322,17 @@ __device__ __forceinline__ int64_t append_slot(const int64_t* slot_mapping, int 
   return slot_mapping != nullptr ? ((const const_i64*)slot_mapping)[s] : -1;   // scalar load
 }
 
-// Places the cursor on chunk c (the first chunk of a worker's range).
+// Places the cursor on the first chunk of a worker's range.
 __device__ __forceinline__ void cursor_start(Cursor& k, const int32_t* lens, const int64_t* slots,
-                                             int num_seqs, int64_t wseq, int64_t c, int lane) {
-  k.c = c;
-  locate_segment(lens, num_seqs, wseq, c, lane, k.h, k.s, k.seg_start);
+                                             const LineSplit& ls) {
+  k.c = ls.b0;
+  k.h = ls.h;
+  k.s = ls.s;
+  k.seg_start = ls.seg_start;
   k.L = ((const const_i32*)lens)[k.s];
   k.slot = append_slot(slots, k.s);
   k.n = chunks_of(k.L);
-  k.j = (int)(c - k.seg_start);
+  k.j = (int)(ls.b0 - k.seg_start);
 }
 
 // Moves the cursor to the next chunk of the line, skipping empty sequences.
@@ -357,6 +420,13 @@ struct StoreQueue {
   lds_u32x4* data;
   lds_u32x4* meta;
   int head, tail;                    // wave-uniform slot counters: [head, tail) queued
+};
+
+// LDS of a decode wave: the split's chunk-count cache is dead once the
+// worker's range is known, and the store queue is used only after that.
+union KernelLds {
+  SplitLds split;
+  QueueLds queue;
 };
 
 __device__ __forceinline__ StoreQueue queue_on(QueueLds& lds) {

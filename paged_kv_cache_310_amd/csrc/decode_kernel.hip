@@ -81,27 +81,17 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
   }
 
   LineSplit ls;
-  if (!split_line(lens, B, HQ, nworkers, w, lane, ls)) {
+  __shared__ KernelLds lds;
+  if (!split_line(lds.split, lens, B, HQ, a.seg_cost, nworkers, w, lane, ls)) {
     if (lane == 0) a.records[w].valid = 0;
     return;
   }
   const int64_t b0 = ls.b0, b1 = ls.b1;
   Cursor cur;
-  cursor_start(cur, lens, a.slot_mapping, B, ls.wseq, b0, lane);
-  if (lane == 0) {
-    // This worker closes the split segment holding b0 if the segment began
-    // in an earlier worker and ends inside this range.
-    MergeRecord r;
-    r.W = ls.W;
-    r.NW = ls.NW;
-    r.seg_start = cur.seg_start;
-    r.first = worker_of(cur.seg_start, ls.W, ls.NW);
-    r.first_slot = cur.seg_start > r.first * ls.W / ls.NW ? 1 : 0;
-    r.seq = cur.s;
-    r.head = cur.h;
-    r.valid = (cur.seg_start < b0 && cur.seg_start + cur.n <= b1) ? 1 : 0;
-    a.records[w] = r;
-  }
+  cursor_start(cur, lens, a.slot_mapping, ls);
+  // This worker closes the split segment holding b0 if the segment began in
+  // an earlier worker and ends inside this range.
+  if (lane == 0) a.records[w] = merge_record(ls, a.seg_cost, cur.n);
 
   const int64_t block_stride = (int64_t)HKV * BS * ROW;
   auto table_of = [&](const Cursor& k) {
@@ -117,15 +107,15 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
     ChunkMeta meta;
   };
 
-  __shared__ QueueLds qlds;
-  StoreQueue q = queue_on(qlds);
+  StoreQueue q = queue_on(lds.queue);
 
-  // Loads the chunk under the cursor, drains kQDrain queued store slots, then
-  // moves the cursor (unless it is on the range's last chunk) and prefetches
-  // the next chunk's block number.  The conditional loads go first: if the
-  // compiler's in-order wait count assumes they were not issued, the extra
-  // wait falls on them, not on this tile's K/V loads.
-  auto issue = [&](Tile& t) {
+  // Loads the chunk under the cursor, drains kQDrain queued store slots (at
+  // one of the ring's two issue sites: the pattern of memory operations stays
+  // fixed), then moves the cursor (unless it is on the range's last chunk)
+  // and prefetches the next chunk's block number.  The conditional loads go
+  // first: if the compiler's in-order wait count assumes they were not
+  // issued, the extra wait falls on them, not on this tile's K/V loads.
+  auto issue = [&](Tile& t, bool drain) {
     t.meta = chunk_meta(cur, b0, b1);
     const int kvh = cur.h / a.group;
     if (t.meta.slot >= 0) {
@@ -147,8 +137,10 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
       t.k[i] = load16(kr, i * 1024 + lane * 16);
       t.v[i] = load16(vr, i * 1024 + lane * 16);
     }
+    if (drain) {
 #pragma unroll
-    for (int d = 0; d < kQDrain; ++d) queue_drain_one(q, lane, a.out);
+      for (int d = 0; d < kQDrain; ++d) queue_drain_one(q, lane, a.out);
+    }
     // Keep the loads ahead of the math on the other tile.
     __builtin_amdgcn_sched_barrier(0);
     if (cur.c + 1 < b1) {
@@ -275,12 +267,12 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
   // loads in flight and segment switches never drain the pipeline.
   const int64_t count = b1 - b0;
   Tile t[2];
-  issue(t[0]);
+  issue(t[0], false);
   for (int64_t i = 0; i < count; i += 2) {
-    issue(t[1]);
+    issue(t[1], true);
     consume(t[0]);
     if (i + 1 >= count) break;
-    issue(t[0]);
+    issue(t[0], false);
     consume(t[1]);
   }
   queue_flush(q, lane, a.out);
@@ -436,6 +428,7 @@ hipError_t launch_decode(const DecodeArgs& args, int dtype, int head_dim, int bl
   DecodeArgs a = args;
   const bool mfma = gqa_supported(dtype, head_dim, a.group);
   a.heads_per_seg = mfma ? a.group : 1;
+  a.seg_cost = mfma ? kSegCostMfma : kSegCostValu;
   hipError_t e = hipSuccess;
   if (before != nullptr && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
   e = mfma ? launch_gqa_attention(a, block_size, workers, stream, nullptr)

@@ -96,25 +96,17 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
   }
 
   LineSplit ls;
-  if (!split_line(lens, B, HKV, nworkers, w, lane, ls)) {
+  __shared__ KernelLds lds;
+  if (!split_line(lds.split, lens, B, HKV, a.seg_cost, nworkers, w, lane, ls)) {
     if (lane == 0) a.records[w].valid = 0;
     return;
   }
   const int64_t b0 = ls.b0, b1 = ls.b1;
   Cursor cur;
-  cursor_start(cur, lens, a.slot_mapping, B, ls.wseq, b0, lane);
-  if (lane == 0) {
-    MergeRecord r;
-    r.W = ls.W;
-    r.NW = ls.NW;
-    r.seg_start = cur.seg_start;
-    r.first = worker_of(cur.seg_start, ls.W, ls.NW);
-    r.first_slot = cur.seg_start > r.first * ls.W / ls.NW ? 1 : 0;
-    r.seq = cur.s;
-    r.head = cur.h;
-    r.valid = (cur.seg_start < b0 && cur.seg_start + cur.n <= b1) ? 1 : 0;
-    a.records[w] = r;
-  }
+  cursor_start(cur, lens, a.slot_mapping, ls);
+  // This worker closes the split segment holding b0 if the segment began in
+  // an earlier worker and ends inside this range.
+  if (lane == 0) a.records[w] = merge_record(ls, a.seg_cost, cur.n);
 
   const int64_t block_stride = (int64_t)HKV * BS * kRow;
   const bool real_head = n < G;
@@ -134,17 +126,17 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
     ChunkMeta meta;
   };
 
-  __shared__ QueueLds qlds;
-  StoreQueue q = queue_on(qlds);
+  StoreQueue q = queue_on(lds.queue);
 
-  // Every tile issues the same tile loads and queue stores (a fixed count
-  // keeps the compiler's in-order wait counts exact).  Rows past the chunk's
+  // Every tile issues the same tile loads, and one of the ring's issue sites
+  // the queue's store (a fixed pattern keeps the compiler's in-order wait
+  // counts exact).  Rows past the chunk's
   // valid tokens lie outside the tile's buffer range and read as 0.  The
   // newest token's rows, loaded only with a segment's last chunk, go first:
   // a wait count that assumes they were not issued then waits for them, not
   // for this tile.  Past the end of the range the cursor stays on the last
   // chunk: such issues reload it and are never consumed.
-  auto issue = [&](Tile& t) {
+  auto issue = [&](Tile& t, bool drain) {
     t.meta = chunk_meta(cur, b0, b1);
     if (t.meta.slot >= 0) {
       const size_t row = ((size_t)cur.s * HKV + cur.h) * kRow;
@@ -168,8 +160,10 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
     for (int i = 0; i < 4; ++i) t.v[i] = load16(vr, i * 1024 + lane * 16);
 #pragma unroll
     for (int k = 0; k < 4; ++k) t.q[k] = load16(qr, qoff + k * 64);
+    if (drain) {
 #pragma unroll
-    for (int d = 0; d < kQDrain; ++d) queue_drain_one(q, lane, a.out);
+      for (int d = 0; d < kQDrain; ++d) queue_drain_one(q, lane, a.out);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (cur.c + 1 < b1) {
       cursor_next(cur, lens, a.slot_mapping, B);
@@ -303,12 +297,12 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
   const int64_t count = b1 - b0;
   Tile t[kRing];
 #pragma unroll
-  for (int r = 0; r + 1 < kRing; ++r) issue(t[r]);
+  for (int r = 0; r + 1 < kRing; ++r) issue(t[r], false);
   for (int64_t i = 0; i < count; i += kRing) {
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
       if (r > 0 && i + r >= count) break;
-      issue(t[(r + kRing - 1) % kRing]);
+      issue(t[(r + kRing - 1) % kRing], r == 0);
       consume(t[r]);
     }
   }

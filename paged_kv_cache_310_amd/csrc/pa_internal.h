@@ -33,6 +33,11 @@ struct MergeRecord {
 
 static_assert(sizeof(MergeRecord) == 48, "merge record layout");
 
+// Work units a segment costs in the split besides its chunks (one unit per
+// chunk), per attention kernel: measured per-segment time over per-chunk time.
+constexpr int kSegCostValu = 1;
+constexpr int kSegCostMfma = 2;
+
 // Everything the decode kernels read, in one POD passed by value.
 struct DecodeArgs {
   void* out;
@@ -52,6 +57,7 @@ struct DecodeArgs {
   int num_kv_heads;
   int group;                  // num_q_heads / num_kv_heads
   int heads_per_seg;          // query heads one work segment covers (1, or group on MFMA)
+  int seg_cost;               // work units a segment costs besides its chunks
   float scale_log2;           // scale * log2(e): scores live in the exp2 domain
 };
 
