@@ -32,11 +32,21 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: achieved HBM GB/s (KV read) & % of peak; seq-steps/sec"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, vendor specification
-DECODE_KERNEL = "decode_valu_kernel"
-# Sources the decode kernel is built from; counter figures taken on other
+# Sources the decode kernels are built from; counter figures taken on other
 # versions of them are not reported.
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_310_amd", "csrc", f)
-                  for f in ("decode_kernel.hip", "decode_common.h", "pa_internal.h")]
+                  for f in ("decode_kernel.hip", "gqa_kernel.hip", "decode_common.h",
+                            "pa_internal.h")]
+
+
+def attention_kernel_name(w) -> str:
+    """The attention kernel pa_decode launches for this workload: the
+    matrix-core kernel for bf16 head_dim 128 with 2..16 query heads per KV
+    head, else the vector kernel."""
+    group = w.num_q_heads // w.num_kv_heads
+    if w.dtype == "bf16" and w.head_dim == 128 and 2 <= group <= 16:
+        return "decode_gqa_kernel"
+    return "decode_valu_kernel"
 
 
 def log(*a):
@@ -246,7 +256,7 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": DECODE_KERNEL, "kernel_source_sha256_16": kernel_source_hash(),
+            "kernel": attention_kernel_name(w), "kernel_source_sha256_16": kernel_source_hash(),
         },
         "device": torch.cuda.get_device_name(dev),
         "host": platform.node(),
