@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       t.k[i] = load16(kr, i * 1024 + lane * 16);
-      t.v[i] = load16(vr, i * 1024 + lane * 16);
+      t.v[i] = load16_stream(vr, i * 1024 + lane * 16);
     }
     if (drain) {
 #pragma unroll

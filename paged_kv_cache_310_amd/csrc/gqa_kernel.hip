@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) t.k[k] = load16(kr, krow_off + k * 64);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = load16(vr, i * 1024 + lane * 16);
+    for (int i = 0; i < 4; ++i) t.v[i] = load16_stream(vr, i * 1024 + lane * 16);
 #pragma unroll
     for (int k = 0; k < 4; ++k) t.q[k] = load16(qr, qoff + k * 64);
     if (drain) {
