@@ -185,6 +185,24 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t x, int lane) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP row operations: shifts
+// within each 16-lane row, then the rows' totals broadcast into the rows
+// above (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).
+// Six VALU steps instead of the LDS-crossbar round trips of a shuffle scan.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_or_zero(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xf, true);
+}
+__device__ __forceinline__ int wave_inclusive_scan32(int x) {
+  x += dpp_or_zero<0x111, 0xf>(x);   // row_shr:1
+  x += dpp_or_zero<0x112, 0xf>(x);   // row_shr:2
+  x += dpp_or_zero<0x114, 0xf>(x);   // row_shr:4
+  x += dpp_or_zero<0x118, 0xf>(x);   // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);   // row_bcast:15
+  x += dpp_or_zero<0x143, 0xc>(x);   // row_bcast:31
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // Work split.
 //
@@ -197,10 +215,10 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t x, int lane) {
 // overhead units followed by one unit per chunk; a worker owns the chunks
 // whose units fall in its unit range.  With seg_cost = 0 the split is an
 // equal split of chunks.
-constexpr int kLenCache = 4096;   // sequences whose chunk counts are cached in LDS
+constexpr int kLenCache = 4096;   // sequences whose lengths are cached in LDS
 
 struct SplitLds {
-  int32_t n[kLenCache];           // chunks of sequence s
+  int32_t len[kLenCache];         // context length of sequence s
 };
 
 struct LineSplit {
@@ -214,8 +232,12 @@ struct LineSplit {
   int64_t seg_unit;     // its first unit
 };
 
+// Length of sequence s: from the LDS cache the split filled, else from memory.
+__device__ __forceinline__ int seq_len(const SplitLds& C, const int32_t* lens, int s) {
+  return s < kLenCache ? ((const lds_i32*)C.len)[s] : lens[s];
+}
 __device__ __forceinline__ int seq_chunks(const SplitLds& C, const int32_t* lens, int s) {
-  return s < kLenCache ? ((const lds_i32*)C.n)[s] : chunks_of(lens[s]);
+  return chunks_of(seq_len(C, lens, s));
 }
 
 // Worker that owns unit u of the line [0, U) split over nw workers.
@@ -223,45 +245,56 @@ __device__ __forceinline__ int64_t worker_of(int64_t u, int64_t U, int64_t nw) {
   return ((u + 1) * nw + U - 1) / U - 1;
 }
 
-// The first chunk whose unit is >= u (W if none), and its segment.
-__device__ void locate_unit(const SplitLds& C, const int32_t* lens, int num_seqs, int seg_cost,
-                            const LineSplit& ls, int64_t u, int lane, int64_t& c, int& h, int& s,
-                            int64_t& seg_start, int64_t& seg_unit) {
-  c = ls.W;
-  h = 0;
-  s = 0;
-  seg_start = ls.W;
-  seg_unit = ls.U;
-  if (u >= ls.U) return;
-  h = (int)(u / ls.useq);
-  const int64_t r = u - (int64_t)h * ls.useq;
-  int64_t acc_u = 0, acc_c = 0;
-  for (int base = 0; base < num_seqs; base += 64) {
+// Where unit target r (relative to the start of its head's units) falls:
+// the first chunk at or after it and its segment.
+struct UnitHit {
+  bool found;
+  int s;
+  int64_t bu, bc;   // units / chunks of the head before sequence s
+  int64_t off;      // r - bu
+};
+
+// Finds the sequences holding unit targets r0 and r1 (each relative to the
+// start of its head's units; every head's units are laid out alike) in one
+// pass over the sequences, 64 at a time.  A sequence of n chunks has
+// n + seg_cost units (0 when empty).
+__device__ void locate_units(const SplitLds& C, const int32_t* lens, int num_seqs, int seg_cost,
+                             int64_t r0, int64_t r1, int lane, UnitHit& h0, UnitHit& h1) {
+  h0.found = false;
+  h1.found = false;
+  int64_t acc_u = 0, acc_ne = 0;
+  for (int base = 0; base < num_seqs && !(h0.found && h1.found); base += 64) {
     const int sq = base + lane;
-    const int64_t n = sq < num_seqs ? seq_chunks(C, lens, sq) : 0;
-    const int64_t un = n > 0 ? n + seg_cost : 0;
-    const int64_t incl_u = wave_inclusive_scan(un, lane);
-    const int64_t incl_c = wave_inclusive_scan(n, lane);
-    const int64_t tot_u = uniform((int64_t)__shfl(incl_u, 63));
-    if (r < acc_u + tot_u) {
-      const unsigned long long hit = __ballot(acc_u + incl_u > r);
-      const int first = __ffsll((long long)hit) - 1;
-      s = uniform(base + first);
-      const int64_t bu = uniform((int64_t)(acc_u + __shfl(incl_u - un, first)));
-      const int64_t bc = uniform((int64_t)(acc_c + __shfl(incl_c - n, first)));
-      const int64_t off = r - bu;
-      seg_start = (int64_t)h * ls.wseq + bc;
-      seg_unit = (int64_t)h * ls.useq + bu;
-      c = seg_start + (off < seg_cost ? 0 : off - seg_cost);
-      return;
+    const int n = sq < num_seqs ? seq_chunks(C, lens, sq) : 0;
+    const int un = n > 0 ? n + seg_cost : 0;
+    const unsigned long long ne = __ballot(n > 0);
+    int64_t incl;
+    if (__ballot(un >= (1 << 24)) == 0) {
+      incl = wave_inclusive_scan32(un);   // the 64 values sum below 2^31
+    } else {
+      incl = wave_inclusive_scan((int64_t)un, lane);
     }
-    acc_u += tot_u;
-    acc_c += uniform((int64_t)__shfl(incl_c, 63));
+    const int64_t tot = uniform((int64_t)__shfl(incl, 63));
+    auto probe = [&](int64_t r, UnitHit& hit) {
+      if (hit.found || r >= acc_u + tot) return;
+      const unsigned long long above = __ballot(acc_u + incl > r);
+      const int first = __ffsll((long long)above) - 1;
+      hit.found = true;
+      hit.s = uniform(base + first);
+      hit.bu = uniform((int64_t)(acc_u + __shfl(incl - un, first)));
+      const int64_t ne_before = acc_ne + __popcll(ne & ((1ull << first) - 1));
+      hit.bc = hit.bu - (int64_t)seg_cost * ne_before;
+      hit.off = r - hit.bu;
+    };
+    probe(r0, h0);
+    probe(r1, h1);
+    acc_u += tot;
+    acc_ne += __popcll(ne);
   }
 }
 
 // Computes the split for worker w; false when w has no chunks.  Caches the
-// sequences' chunk counts in C on the way.
+// sequences' lengths in C on the way.
 __device__ __forceinline__ bool split_line(SplitLds& C, const int32_t* lens, int num_seqs,
                                            int num_heads, int seg_cost, int nworkers, int w,
                                            int lane, LineSplit& ls) {
@@ -272,8 +305,9 @@ __device__ __forceinline__ bool split_line(SplitLds& C, const int32_t* lens, int
     for (int k = 0; k < 4; ++k) {
       const int sq = base + k * 64 + lane;
       if (sq < num_seqs) {
-        const int c = chunks_of(lens[sq]);
-        if (sq < kLenCache) ((lds_i32*)C.n)[sq] = c;
+        const int L = lens[sq];
+        if (sq < kLenCache) ((lds_i32*)C.len)[sq] = L;
+        const int c = chunks_of(L);
         n += c;
         un += c > 0 ? c + seg_cost : 0;
       }
@@ -290,11 +324,19 @@ __device__ __forceinline__ bool split_line(SplitLds& C, const int32_t* lens, int
   if (w >= ls.NW) return false;
   ls.u0 = (int64_t)w * ls.U / ls.NW;
   ls.u1 = (int64_t)(w + 1) * ls.U / ls.NW;
-  int h1, s1;
-  int64_t st1, su1;
-  locate_unit(C, lens, num_seqs, seg_cost, ls, ls.u0, lane, ls.b0, ls.h, ls.s, ls.seg_start,
-              ls.seg_unit);
-  locate_unit(C, lens, num_seqs, seg_cost, ls, ls.u1, lane, ls.b1, h1, s1, st1, su1);
+  // Both ends of the range in one pass; u1 == U is the line's end.
+  const int hh0 = (int)(ls.u0 / ls.useq);
+  const int hh1 = ls.u1 < ls.U ? (int)(ls.u1 / ls.useq) : 0;
+  const int64_t r1 = ls.u1 < ls.U ? ls.u1 - (int64_t)hh1 * ls.useq : ls.U;
+  UnitHit x0, x1;
+  locate_units(C, lens, num_seqs, seg_cost, ls.u0 - (int64_t)hh0 * ls.useq, r1, lane, x0, x1);
+  ls.h = hh0;
+  ls.s = x0.s;
+  ls.seg_start = (int64_t)hh0 * ls.wseq + x0.bc;
+  ls.seg_unit = (int64_t)hh0 * ls.useq + x0.bu;
+  ls.b0 = ls.seg_start + (x0.off < seg_cost ? 0 : x0.off - seg_cost);
+  ls.b1 = ls.u1 < ls.U ? (int64_t)hh1 * ls.wseq + x1.bc + (x1.off < seg_cost ? 0 : x1.off - seg_cost)
+                       : ls.W;
   return ls.b0 < ls.b1;
 }
 
@@ -331,13 +373,13 @@ __device__ __forceinline__ int64_t append_slot(const int64_t* slot_mapping, int 
 }
 
 // Places the cursor on the first chunk of a worker's range.
-__device__ __forceinline__ void cursor_start(Cursor& k, const int32_t* lens, const int64_t* slots,
-                                             const LineSplit& ls) {
+__device__ __forceinline__ void cursor_start(Cursor& k, const SplitLds& C, const int32_t* lens,
+                                             const int64_t* slots, const LineSplit& ls) {
   k.c = ls.b0;
   k.h = ls.h;
   k.s = ls.s;
   k.seg_start = ls.seg_start;
-  k.L = ((const const_i32*)lens)[k.s];
+  k.L = uniform(seq_len(C, lens, k.s));
   k.slot = append_slot(slots, k.s);
   k.n = chunks_of(k.L);
   k.j = (int)(ls.b0 - k.seg_start);
@@ -491,6 +533,18 @@ __device__ __forceinline__ void queue_job(const StoreQueue& q, int first, const 
     const int b = bytes - lane * 1024 < 1024 ? bytes - lane * 1024 : 1024;
     q.meta[(first + lane) & (kQSlots - 1)] = u32x4{(uint32_t)d, (uint32_t)(d >> 32), (uint32_t)b, 0u};
   }
+}
+
+// Queues a worker's 48-byte merge record (lanes 0..2 carry 16 bytes each).
+__device__ __forceinline__ void queue_record(StoreQueue& q, MergeRecord* dst, const MergeRecord& r,
+                                             int lane, const void* any) {
+  static_assert(sizeof(MergeRecord) == 48, "three 16-byte pieces");
+  u32x4 p[3];
+  __builtin_memcpy(p, &r, sizeof(p));
+  const int f = queue_reserve(q, 1, lane, any);
+  const u32x4 mine = lane == 0 ? p[0] : lane == 1 ? p[1] : p[2];
+  if (lane < 3) queue_put(q, f, lane * 16, mine);
+  queue_job(q, f, dst, (int)sizeof(MergeRecord), lane);
 }
 
 // Stores everything still queued (end of the worker's range).

@@ -88,25 +88,25 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
   const int G = a.group;
   const int32_t* __restrict__ lens = a.context_lens;
 
+
+  LineSplit ls;
+  __shared__ KernelLds lds;
+  const bool has_chunks = split_line(lds.split, lens, B, HKV, a.seg_cost, nworkers, w, lane, ls);
+  // Sequences with no cached token produce zero rows (lengths from the
+  // split's LDS cache).
   for (int s = w; s < B; s += nworkers) {
-    if (lens[s] == 0) {
+    if (seq_len(lds.split, lens, s) == 0) {
       uint4* o = reinterpret_cast<uint4*>(static_cast<char*>(a.out) + (size_t)s * HQ * kRow);
       for (int u = lane; u < HQ * (kRow / 16); u += 64) o[u] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
-
-  LineSplit ls;
-  __shared__ KernelLds lds;
-  if (!split_line(lds.split, lens, B, HKV, a.seg_cost, nworkers, w, lane, ls)) {
+  if (!has_chunks) {
     if (lane == 0) a.records[w].valid = 0;
     return;
   }
   const int64_t b0 = ls.b0, b1 = ls.b1;
   Cursor cur;
-  cursor_start(cur, lens, a.slot_mapping, ls);
-  // This worker closes the split segment holding b0 if the segment began in
-  // an earlier worker and ends inside this range.
-  if (lane == 0) a.records[w] = merge_record(ls, a.seg_cost, cur.n);
+  cursor_start(cur, lds.split, lens, a.slot_mapping, ls);
 
   const int64_t block_stride = (int64_t)HKV * BS * kRow;
   const bool real_head = n < G;
@@ -127,6 +127,11 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
   };
 
   StoreQueue q = queue_on(lds.queue);
+  // This worker closes the split segment holding b0 if the segment began in
+  // an earlier worker and ends inside this range.  The record goes out
+  // through the store queue: a plain store ahead of the first tile would make
+  // the first tile's wait include its acknowledgement.
+  queue_record(q, a.records + w, merge_record(ls, a.seg_cost, cur.n), lane, a.out);
 
   // Every tile issues the same tile loads, and one of the ring's issue sites
   // the queue's store (a fixed pattern keeps the compiler's in-order wait

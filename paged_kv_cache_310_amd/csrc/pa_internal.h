@@ -34,8 +34,9 @@ struct MergeRecord {
 static_assert(sizeof(MergeRecord) == 48, "merge record layout");
 
 // Work units a segment costs in the split besides its chunks (one unit per
-// chunk), per attention kernel: measured per-segment time over per-chunk time.
-constexpr int kSegCostValu = 1;
+// chunk), per attention kernel: about the measured per-segment time over the
+// per-chunk time, then tuned by timing.
+constexpr int kSegCostValu = 2;
 constexpr int kSegCostMfma = 2;
 
 // Everything the decode kernels read, in one POD passed by value.
