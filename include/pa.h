@@ -6,6 +6,9 @@
  *   pa_copy_blocks  copy whole blocks (the copy in copy-on-write);
  *   pa_decode       one decode step of attention for every sequence, reading each
  *                   sequence's keys/values through its block table.
+ * and, for a model whose layers each own a pool, layer-batched forms of the
+ * first two (pa_append_kv_layers, pa_copy_blocks_layers): one call serves
+ * every layer.
  *
  * Sources: the pages on "Efficient Memory Management for Large Language Model
  * Serving with PagedAttention" -- zeroshotmind.com essay, sections "Paging the
@@ -84,6 +87,41 @@ int pa_append_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int64_t num_pairs,
                    int64_t num_blocks, int num_kv_heads, int block_size, int head_dim,
                    int dtype, void* stream);
+
+/* Layer-batched append.  Each layer of a model caches its own keys and
+ * values, all under one block table per sequence (pages: "Paging the cache",
+ * "Block tables: logical order, physical scatter" -- a token's slot is chosen
+ * once, so every layer writes the same slot of its own pool).  For every layer
+ * l in [0, num_layers) this does exactly what
+ *   pa_append_kv(k_caches[l], v_caches[l], k_new[l], v_new[l], slot_mapping, ...)
+ * does, in one launch per 32 layers instead of one per layer.
+ *   k_caches, v_caches  HOST arrays of num_layers device pointers to pools
+ *                       [num_blocks, num_kv_heads, block_size, head_dim]
+ *   k_new, v_new        HOST arrays of num_layers device pointers to
+ *                       [num_tokens, num_kv_heads, head_dim]
+ *   slot_mapping        int64 [num_tokens], device, shared by all layers
+ * The host arrays are read during the call only.  Every pointer in them must
+ * be non-NULL and 16-byte aligned (else PA_ERR_INVALID); pools of different
+ * layers must not overlap.  num_tokens == 0 or num_layers == 0 is a no-op.
+ * Same slot contract and PA_CHECK behaviour as pa_append_kv. */
+int pa_append_kv_layers(void* const* k_caches, void* const* v_caches,
+                        const void* const* k_new, const void* const* v_new, int num_layers,
+                        const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                        int num_kv_heads, int block_size, int head_dim, int dtype, void* stream);
+
+/* Layer-batched copy-on-write copy (page: "Sharing a prefix without copying
+ * it"): a shared block is shared in every layer's pool at once, so its
+ * duplication copies the block in every layer.  For every layer l this does
+ * exactly what pa_copy_blocks(k_caches[l], v_caches[l], block_mapping, ...)
+ * does, in one launch per 32 layers (and per 65535 pairs).
+ *   k_caches, v_caches  HOST arrays of num_layers device pointers to pools
+ *   block_mapping       int64 [num_pairs][2] = (src, dst), device, shared by all layers
+ * Pointer rules as pa_append_kv_layers; copy-pair contract and PA_CHECK
+ * behaviour as pa_copy_blocks.  num_pairs == 0 or num_layers == 0 is a no-op. */
+int pa_copy_blocks_layers(void* const* k_caches, void* const* v_caches, int num_layers,
+                          const int64_t* block_mapping, int64_t num_pairs, int64_t num_blocks,
+                          int num_kv_heads, int block_size, int head_dim, int dtype,
+                          void* stream);
 
 /* Bytes of device workspace pa_decode needs for these sizes and `num_workers`
  * (0 = the library's default for the current device).  Writes *bytes.  The

@@ -58,6 +58,11 @@ def _load():
         lib.pa_append_kv.restype = i32
         lib.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp]
         lib.pa_copy_blocks.restype = i32
+        lib.pa_append_kv_layers.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, i32, i32, i32,
+                                            i32, vp]
+        lib.pa_append_kv_layers.restype = i32
+        lib.pa_copy_blocks_layers.argtypes = [vp, vp, i32, vp, i64, i64, i32, i32, i32, i32, vp]
+        lib.pa_copy_blocks_layers.restype = i32
         lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         lib.pa_decode_workspace_size.restype = i32
         lib.pa_decode_default_workers.argtypes = [ctypes.POINTER(i32)]
@@ -132,6 +137,57 @@ def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
     _call("pa_copy_blocks", _load().pa_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), block_mapping.numel() // 2, nb, hkv, bs,
         d, _dtype_code(k_cache), _stream(k_cache.device, stream)))
+
+
+def _layer_pools(k_caches, v_caches):
+    """Checks per-layer pools (same shape, dtype, device) and returns their
+    shape and host arrays of their device pointers."""
+    _need(len(k_caches) == len(v_caches) and len(k_caches) > 0,
+          "k_caches and v_caches must be equally long, non-empty sequences of pools")
+    shape = _check_cache(k_caches[0], v_caches[0])
+    for k, v in zip(k_caches, v_caches):
+        _need(_check_cache(k, v) == shape and k.dtype == k_caches[0].dtype
+              and k.device == k_caches[0].device, "every layer's pools must match layer 0's")
+    return shape, _ptr_array(k_caches), _ptr_array(v_caches)
+
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def pa_append_kv_layers(k_caches, v_caches, k_new, v_new, slot_mapping, stream=None) -> None:
+    """``pa_append_kv`` for every layer ``l`` (pools ``k_caches[l]``,
+    ``v_caches[l]``, new rows ``k_new[l]``, ``v_new[l]``), one slot mapping for
+    all layers, in one launch per 32 layers."""
+    (nb, hkv, bs, d), kp, vp = _layer_pools(k_caches, v_caches)
+    layers = len(k_caches)
+    ref = k_caches[0]
+    t = slot_mapping.numel()
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+          and slot_mapping.device == ref.device, "slot_mapping must be int64 on the pool device")
+    _need(len(k_new) == layers and len(v_new) == layers, "one k_new and one v_new per layer")
+    for x in list(k_new) + list(v_new):
+        _need(x.shape == (t, hkv, d) and x.dtype == ref.dtype and x.is_contiguous()
+              and x.device == ref.device, "k_new/v_new must be [num_tokens, num_kv_heads, head_dim]")
+    _call("pa_append_kv_layers", _load().pa_append_kv_layers(
+        kp, vp, _ptr_array(k_new), _ptr_array(v_new), layers, _ptr(slot_mapping), t, nb, hkv, bs,
+        d, _dtype_code(ref), _stream(ref.device, stream)))
+
+
+def pa_copy_blocks_layers(k_caches, v_caches, block_mapping, stream=None) -> None:
+    """``pa_copy_blocks`` for every layer's pools, one pair list for all
+    layers, in one launch per 32 layers."""
+    (nb, hkv, bs, d), kp, vp = _layer_pools(k_caches, v_caches)
+    ref = k_caches[0]
+    _need(block_mapping.dtype == torch.int64 and block_mapping.is_contiguous()
+          and block_mapping.device == ref.device and block_mapping.numel() % 2 == 0,
+          "block_mapping must be int64 [num_pairs, 2] on the pool device")
+    _call("pa_copy_blocks_layers", _load().pa_copy_blocks_layers(
+        kp, vp, len(k_caches), _ptr(block_mapping), block_mapping.numel() // 2, nb, hkv, bs, d,
+        _dtype_code(ref), _stream(ref.device, stream)))
 
 
 def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

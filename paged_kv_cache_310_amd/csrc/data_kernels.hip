@@ -64,6 +64,63 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(
   }
 }
 
+// Multi-layer variants: the pools of up to kMaxLayersPerLaunch layers travel
+// by value in the kernel arguments, so one launch serves every layer without
+// a device-side pointer table.
+struct LayerPools {
+  char* k[kMaxLayersPerLaunch];
+  char* v[kMaxLayersPerLaunch];
+  const char* k_new[kMaxLayersPerLaunch];
+  const char* v_new[kMaxLayersPerLaunch];
+};
+
+// grid: x covers the units of one layer's rows, y = layer.
+__global__ __launch_bounds__(256) void append_layers_kernel(
+    const LayerPools p, const int64_t* __restrict__ slot_mapping, int64_t num_units,
+    int num_kv_heads, int block_size, int row_units) {
+  const int64_t unit = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (unit >= num_units) return;
+  const int layer = blockIdx.y;
+  const int u = (int)(unit % row_units);
+  const int64_t row = unit / row_units;            // token * num_kv_heads + head
+  const int head = (int)(row % num_kv_heads);
+  const int64_t token = row / num_kv_heads;
+  const int64_t slot = slot_mapping[token];
+  if (slot < 0) return;
+  const int64_t block = slot / block_size;
+  const int64_t offset = slot - block * block_size;
+  const int64_t dst = (((block * num_kv_heads + head) * block_size + offset) * row_units + u);
+  const int64_t src = row * row_units + u;
+  const uint4 kv = reinterpret_cast<const uint4*>(p.k_new[layer])[src];
+  const uint4 vv = reinterpret_cast<const uint4*>(p.v_new[layer])[src];
+  reinterpret_cast<uint4*>(p.k[layer])[dst] = kv;
+  reinterpret_cast<uint4*>(p.v[layer])[dst] = vv;
+}
+
+// grid: x = piece of the block, y = pair, z = 2 * layer + (0 K / 1 V).
+__global__ __launch_bounds__(kCopyThreads) void copy_layers_kernel(
+    const LayerPools p, const int64_t* __restrict__ block_mapping, int64_t block_units) {
+  const int64_t pair = blockIdx.y;
+  const int layer = blockIdx.z >> 1;
+  const int64_t src = block_mapping[2 * pair];
+  const int64_t dst = block_mapping[2 * pair + 1];
+  uint4* pool = reinterpret_cast<uint4*>((blockIdx.z & 1) == 0 ? p.k[layer] : p.v[layer]);
+  const uint4* from = pool + src * block_units;
+  uint4* to = pool + dst * block_units;
+  const int64_t first = (int64_t)blockIdx.x * (kCopyThreads * kCopyUnroll) + threadIdx.x;
+  uint4 buf[kCopyUnroll];
+#pragma unroll
+  for (int i = 0; i < kCopyUnroll; ++i) {
+    const int64_t u = first + i * kCopyThreads;
+    if (u < block_units) buf[i] = from[u];
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyUnroll; ++i) {
+    const int64_t u = first + i * kCopyThreads;
+    if (u < block_units) to[u] = buf[i];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
@@ -95,6 +152,58 @@ hipError_t launch_copy(void* k_cache, void* v_cache, const int64_t* block_mappin
                        block_mapping + 2 * first, units);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_append_layers(void* const* k_caches, void* const* v_caches,
+                                const void* const* k_new, const void* const* v_new, int num_layers,
+                                const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                                int block_size, int row_bytes, hipStream_t stream) {
+  const int row_units = row_bytes / 16;
+  const int64_t units = num_tokens * num_kv_heads * row_units;
+  const int threads = 256;
+  const int64_t blocks = (units + threads - 1) / threads;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  for (int first = 0; first < num_layers; first += kMaxLayersPerLaunch) {
+    const int n = num_layers - first < kMaxLayersPerLaunch ? num_layers - first : kMaxLayersPerLaunch;
+    LayerPools p{};
+    for (int l = 0; l < n; ++l) {
+      p.k[l] = static_cast<char*>(k_caches[first + l]);
+      p.v[l] = static_cast<char*>(v_caches[first + l]);
+      p.k_new[l] = static_cast<const char*>(k_new[first + l]);
+      p.v_new[l] = static_cast<const char*>(v_new[first + l]);
+    }
+    hipLaunchKernelGGL(append_layers_kernel, dim3((unsigned)blocks, (unsigned)n), dim3(threads), 0,
+                       stream, p, slot_mapping, units, num_kv_heads, block_size, row_units);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_copy_layers(void* const* k_caches, void* const* v_caches, int num_layers,
+                              const int64_t* block_mapping, int64_t num_pairs, int64_t block_bytes,
+                              hipStream_t stream) {
+  const int64_t units = block_bytes / 16;
+  const int64_t per_wg = kCopyThreads * kCopyUnroll;
+  const int64_t gx = (units + per_wg - 1) / per_wg;
+  if (gx > INT32_MAX) return hipErrorInvalidValue;
+  const int64_t kMaxY = 65535;   // grid y limit: launch in batches of pairs
+  for (int first = 0; first < num_layers; first += kMaxLayersPerLaunch) {
+    const int n = num_layers - first < kMaxLayersPerLaunch ? num_layers - first : kMaxLayersPerLaunch;
+    LayerPools p{};
+    for (int l = 0; l < n; ++l) {
+      p.k[l] = static_cast<char*>(k_caches[first + l]);
+      p.v[l] = static_cast<char*>(v_caches[first + l]);
+    }
+    for (int64_t pf = 0; pf < num_pairs; pf += kMaxY) {
+      const int64_t np = num_pairs - pf < kMaxY ? num_pairs - pf : kMaxY;
+      hipLaunchKernelGGL(copy_layers_kernel, dim3((unsigned)gx, (unsigned)np, (unsigned)(2 * n)),
+                         dim3(kCopyThreads), 0, stream, p, block_mapping + 2 * pf, units);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

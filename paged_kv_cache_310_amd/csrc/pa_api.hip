@@ -42,6 +42,47 @@ bool copy_to_host(std::vector<I>& dst, const I* src, size_t n, hipStream_t strea
   return hipStreamSynchronize(stream) == hipSuccess;
 }
 
+// PA_CHECK: every non-negative slot lies in the pool and none repeats.
+int validate_slots(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,
+                   hipStream_t st) {
+  std::vector<int64_t> slots;
+  if (!copy_to_host(slots, slot_mapping, (size_t)num_tokens, st)) return PA_ERR_HIP;
+  std::vector<char> seen((size_t)num_slots, 0);
+  for (int64_t s : slots) {
+    if (s < 0) continue;
+    if (s >= num_slots || seen[(size_t)s]) return PA_ERR_INDEX;
+    seen[(size_t)s] = 1;
+  }
+  return PA_OK;
+}
+
+// PA_CHECK: pairs in range, no destination repeats or is also a source.
+int validate_pairs(const int64_t* block_mapping, int64_t num_pairs, int64_t num_blocks,
+                   hipStream_t st) {
+  std::vector<int64_t> pairs;
+  if (!copy_to_host(pairs, block_mapping, (size_t)(2 * num_pairs), st)) return PA_ERR_HIP;
+  std::vector<char> role((size_t)num_blocks, 0);   // 1 = src, 2 = dst
+  for (int64_t p = 0; p < num_pairs; ++p) {
+    const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return PA_ERR_INDEX;
+    if (role[(size_t)dst] != 0) return PA_ERR_INDEX;   // dst repeats or is a src
+    if (role[(size_t)src] == 2) return PA_ERR_INDEX;   // src is an earlier dst
+    role[(size_t)src] = 1;
+    role[(size_t)dst] = 2;
+  }
+  return PA_OK;
+}
+
+// Every entry of a host array of num_layers device pointers is non-null and
+// 16-byte aligned.
+template <typename P>
+bool layer_pointers_ok(const P* ptrs, int num_layers) {
+  if (!ptrs) return false;
+  for (int l = 0; l < num_layers; ++l)
+    if (!ptrs[l] || !aligned16(ptrs[l])) return false;
+  return true;
+}
+
 // Compute units of the current device (cached per device).
 int current_device_cus(int* out) {
   static std::mutex mu;
@@ -123,14 +164,8 @@ int pa_append_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_
     return PA_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (check_enabled()) {
-    std::vector<int64_t> slots;
-    if (!copy_to_host(slots, slot_mapping, (size_t)num_tokens, st)) return PA_ERR_HIP;
-    std::vector<char> seen((size_t)(num_blocks * block_size), 0);
-    for (int64_t s : slots) {
-      if (s < 0) continue;
-      if (s >= num_blocks * block_size || seen[(size_t)s]) return PA_ERR_INDEX;
-      seen[(size_t)s] = 1;
-    }
+    const int vs = validate_slots(slot_mapping, num_tokens, num_blocks * block_size, st);
+    if (vs != PA_OK) return vs;
   }
   const int row_bytes = head_dim * pa::elem_bytes(dtype);
   return pa::launch_append(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens, num_kv_heads,
@@ -151,21 +186,65 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (check_enabled()) {
-    std::vector<int64_t> pairs;
-    if (!copy_to_host(pairs, block_mapping, (size_t)(2 * num_pairs), st)) return PA_ERR_HIP;
-    std::vector<char> role((size_t)num_blocks, 0);   // 1 = src, 2 = dst
-    for (int64_t p = 0; p < num_pairs; ++p) {
-      const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
-      if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return PA_ERR_INDEX;
-      if (role[(size_t)dst] != 0) return PA_ERR_INDEX;   // dst repeats or is a src
-      if (role[(size_t)src] == 2) return PA_ERR_INDEX;   // src is an earlier dst
-      role[(size_t)src] = 1;
-      role[(size_t)dst] = 2;
-    }
+    const int vp = validate_pairs(block_mapping, num_pairs, num_blocks, st);
+    if (vp != PA_OK) return vp;
   }
   const int64_t block_bytes =
       (int64_t)num_kv_heads * block_size * head_dim * pa::elem_bytes(dtype);
   return pa::launch_copy(k_cache, v_cache, block_mapping, num_pairs, block_bytes, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int pa_append_kv_layers(void* const* k_caches, void* const* v_caches,
+                        const void* const* k_new, const void* const* v_new, int num_layers,
+                        const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                        int num_kv_heads, int block_size, int head_dim, int dtype, void* stream) {
+  if (num_tokens < 0 || num_layers < 0 ||
+      !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks))
+    return PA_ERR_INVALID;
+  const int sup = support_status(dtype, block_size, head_dim);
+  if (sup != PA_OK) return sup;
+  if (num_tokens == 0 || num_layers == 0) return PA_OK;
+  if (!slot_mapping || !layer_pointers_ok(k_caches, num_layers) ||
+      !layer_pointers_ok(v_caches, num_layers) || !layer_pointers_ok(k_new, num_layers) ||
+      !layer_pointers_ok(v_new, num_layers))
+    return PA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    const int vs = validate_slots(slot_mapping, num_tokens, num_blocks * block_size, st);
+    if (vs != PA_OK) return vs;
+  }
+  const int row_bytes = head_dim * pa::elem_bytes(dtype);
+  return pa::launch_append_layers(k_caches, v_caches, k_new, v_new, num_layers, slot_mapping,
+                                  num_tokens, num_kv_heads, block_size, row_bytes,
+                                  st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int pa_copy_blocks_layers(void* const* k_caches, void* const* v_caches, int num_layers,
+                          const int64_t* block_mapping, int64_t num_pairs, int64_t num_blocks,
+                          int num_kv_heads, int block_size, int head_dim, int dtype,
+                          void* stream) {
+  if (num_pairs < 0 || num_layers < 0 ||
+      !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks))
+    return PA_ERR_INVALID;
+  const int sup = support_status(dtype, block_size, head_dim);
+  if (sup != PA_OK) return sup;
+  if (num_pairs == 0 || num_layers == 0) return PA_OK;
+  if (!block_mapping || !layer_pointers_ok(k_caches, num_layers) ||
+      !layer_pointers_ok(v_caches, num_layers))
+    return PA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    const int vp = validate_pairs(block_mapping, num_pairs, num_blocks, st);
+    if (vp != PA_OK) return vp;
+  }
+  const int64_t block_bytes =
+      (int64_t)num_kv_heads * block_size * head_dim * pa::elem_bytes(dtype);
+  return pa::launch_copy_layers(k_caches, v_caches, num_layers, block_mapping, num_pairs,
+                                block_bytes, st) == hipSuccess
              ? PA_OK
              : PA_ERR_HIP;
 }

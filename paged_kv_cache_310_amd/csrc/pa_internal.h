@@ -91,6 +91,18 @@ hipError_t decode_resident_per_cu(int dtype, int head_dim, int block_size, int g
 bool gqa_supported(int dtype, int head_dim, int group);
 hipError_t launch_gqa_attention(const DecodeArgs& a, int block_size, int workers,
                                 hipStream_t stream, int* resident);
+// Layers served by one multi-layer append or copy launch (their pool
+// pointers travel in the kernel arguments).
+constexpr int kMaxLayersPerLaunch = 32;
+
+hipError_t launch_append_layers(void* const* k_caches, void* const* v_caches,
+                                const void* const* k_new, const void* const* v_new, int num_layers,
+                                const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                                int block_size, int row_bytes, hipStream_t stream);
+hipError_t launch_copy_layers(void* const* k_caches, void* const* v_caches, int num_layers,
+                              const int64_t* block_mapping, int64_t num_pairs, int64_t block_bytes,
+                              hipStream_t stream);
+
 hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                          const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
                          int block_size, int row_bytes, hipStream_t stream);

@@ -100,6 +100,36 @@ def test_append_and_copy_reject_bad_scalars(lib):
     assert lib.pa_copy_blocks(FAKE, FAKE, None, 2, 10, 8, 32, 64, 0, None) == 1
 
 
+def _ptrs(*values):
+    arr = (ctypes.c_void_p * max(len(values), 1))()
+    for i, x in enumerate(values):
+        arr[i] = x
+    return arr
+
+
+def test_layer_batched_calls_reject_bad_arguments(lib):
+    three = _ptrs(FAKE, FAKE + 4096, FAKE + 8192)
+    holes = _ptrs(FAKE, None, FAKE)
+    skew = _ptrs(FAKE, FAKE + 8, FAKE)
+    app = lib.pa_append_kv_layers
+    assert app(three, three, three, three, 3, FAKE, 0, 10, 8, 16, 128, 1, None) == 0   # no tokens
+    assert app(three, three, three, three, 0, FAKE, 5, 10, 8, 16, 128, 1, None) == 0   # no layers
+    assert app(three, three, three, three, -1, FAKE, 5, 10, 8, 16, 128, 1, None) == 1
+    assert app(three, three, three, three, 3, FAKE, 5, 10, 8, 16, 96, 1, None) == 2
+    assert app(three, holes, three, three, 3, FAKE, 5, 10, 8, 16, 128, 1, None) == 1
+    assert app(three, three, three, skew, 3, FAKE, 5, 10, 8, 16, 128, 1, None) == 1
+    assert app(None, three, three, three, 3, FAKE, 5, 10, 8, 16, 128, 1, None) == 1
+    assert app(three, three, three, three, 3, None, 5, 10, 8, 16, 128, 1, None) == 1
+    cp = lib.pa_copy_blocks_layers
+    assert cp(three, three, 3, FAKE, 0, 10, 8, 16, 128, 1, None) == 0
+    assert cp(three, three, 0, FAKE, 4, 10, 8, 16, 128, 1, None) == 0
+    assert cp(three, three, 3, FAKE, -2, 10, 8, 16, 128, 1, None) == 1
+    assert cp(three, three, 3, FAKE, 4, 10, 8, 16, 128, 7, None) == 2
+    assert cp(three, holes, 3, FAKE, 4, 10, 8, 16, 128, 1, None) == 1
+    assert cp(skew, three, 3, FAKE, 4, 10, 8, 16, 128, 1, None) == 1
+    assert cp(three, three, 3, None, 4, 10, 8, 16, 128, 1, None) == 1
+
+
 def test_decode_event_hook_arguments(lib):
     assert lib.pa_set_decode_events(FAKE, None) == 1
     assert lib.pa_set_decode_events(None, FAKE) == 1
