@@ -17,4 +17,7 @@ from .paged_attention import (  # noqa: F401
     copy_blocks,
     decode,
     gather_sequence,
+    prefill,
+    query_position,
+    visible_keys,
 )

@@ -1,5 +1,6 @@
 """Plain, slow, obviously-correct CPU oracle for paged decode attention,
-the paged KV append and the copy-on-write block copy.
+paged multi-token (prefill) attention, the paged KV append and the
+copy-on-write block copy.
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may use this module.  It shares no code
@@ -17,6 +18,8 @@ Language Model Serving with PagedAttention"; cited by page and section):
 The pages give no attention formula.  The oracle uses the textbook scaled
 dot-product attention ``softmax(q . K^T * scale) . V`` over every cached
 token of the sequence, including the one written this step (no other mask).
+For a chunk of several query tokens (``prefill``) each query token sees the
+positions up to and including its own (causal attention).
 
 Memory layout read by the oracle (a reading: the pages fix no layout):
 
@@ -172,4 +175,75 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype,
             cached = {key: (k, v)}
         k, v = cached[key]
         out[s, h] = attention_rows(bits_to_f64(q[s, h], dtype), k, v, scale64)
+    return out
+
+
+def query_position(context_len, query_len, i):
+    """Position of the ``i``-th token of a sequence's query chunk.
+
+    A chunk of ``query_len`` query tokens is the sequence's newest tokens:
+    their keys/values are already cached, so the sequence holds
+    ``context_len`` tokens and query token ``i`` sits at position
+    ``context_len - query_len + i``.  (A reading: the pages describe prompt
+    processing only as attention read through the block table -- [P1] method
+    paragraph -- and fix no chunk convention; this is the one a decode step
+    generalises, since a chunk of one token is exactly a decode step.)
+    """
+    return int(context_len) - int(query_len) + int(i)
+
+
+def visible_keys(position):
+    """Number of leading positions a query at ``position`` attends to: every
+    position up to and including its own (causal attention in a decoder)."""
+    return int(position) + 1
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, dtype,
+            block_size, rows=None):
+    """Multi-token (prompt / chunked prompt) paged attention, fp64.
+
+    ``q``: ``[num_query_tokens, num_q_heads, head_dim]`` raw bits; the query
+    tokens of sequence ``s`` are rows ``query_start[s] .. query_start[s+1]-1``
+    (int32 ``query_start`` of length ``num_seqs + 1``).  Their keys/values
+    are already in the pools (written by an append through the slot mapping).
+    Query token ``i`` of sequence ``s`` at position ``p`` attends to the
+    sequence's positions ``0 .. p`` read through its block table:
+    ``out = sum_{j <= p} softmax_j(scale * q . k_j) v_j``.
+
+    [P1] method paragraph: attention kernels read through the block table.
+    [P3] "Block tables": the logical order is the sequence's order, so the
+    result is plain causal attention over the gathered keys and values.
+    ``rows``: optional iterable of ``(query_token, q_head)`` pairs to evaluate
+    (the others stay zero).  Returns fp64 ``[num_query_tokens, num_q_heads,
+    head_dim]``.
+    """
+    num_tokens, num_q_heads, head_dim = q.shape
+    num_kv_heads = k_cache.shape[1]
+    if num_q_heads % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    starts = np.asarray(query_start, dtype=np.int64)
+    seq_of = np.zeros(num_tokens, dtype=np.int64)
+    for s in range(len(starts) - 1):
+        seq_of[starts[s]:starts[s + 1]] = s
+    scale64 = np.float64(np.float32(scale))
+    out = np.zeros((num_tokens, num_q_heads, head_dim), dtype=np.float64)
+    if rows is None:
+        rows = [(t, h) for t in range(num_tokens) for h in range(num_q_heads)]
+    cached = {}
+    for t, h in rows:
+        s = int(seq_of[t])
+        length = int(context_lens[s])
+        n = int(starts[s + 1] - starts[s])
+        position = query_position(length, n, t - starts[s])
+        kv_head = kv_head_for(h, num_q_heads, num_kv_heads)
+        key = (s, kv_head)
+        if key not in cached:
+            k = bits_to_f64(gather_sequence(k_cache, block_tables[s], length,
+                                            block_size, kv_head), dtype)
+            v = bits_to_f64(gather_sequence(v_cache, block_tables[s], length,
+                                            block_size, kv_head), dtype)
+            cached = {key: (k, v)}
+        k, v = cached[key]
+        m = visible_keys(position)
+        out[t, h] = attention_rows(bits_to_f64(q[t, h], dtype), k[:m], v[:m], scale64)
     return out

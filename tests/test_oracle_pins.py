@@ -19,6 +19,11 @@ What pins what:
   result; aliased (shared) prefix blocks equal private copies; a block copy
   duplicates exactly one block and leaves the source untouched; an append
   writes exactly its slot.
+* multi-token (prefill) attention: torch attention with a shifted
+  lower-triangular mask on contiguous K/V; brute-force decodes of the
+  sequence cut after each query position; a fresh prompt's first token gives
+  v0; q = 0 gives the running mean of V; one token per sequence equals the
+  decode; one chunk equals two.
 """
 
 import json
@@ -323,6 +328,111 @@ def check_decode_all(decode):
     check_sharing(decode)
 
 
+# ------------------------------------------------------- multi-token (prefill)
+def prefill_case(rng, ctx, qlens, hq, hkv, d, bs, dtype):
+    """Contiguous K/V of lengths ``ctx`` scattered into a permuted pool, and a
+    query chunk of ``qlens[s]`` tokens per sequence (its newest tokens)."""
+    ks, vs = random_contiguous(rng, ctx, hkv, d, dtype)
+    nb = sum(-(-n // bs) for n in ctx) + 3
+    kp, vp, tab = scatter_into_pool(ks, vs, bs, nb, rng.permutation(nb), nan_fill(dtype))
+    total = int(sum(qlens))
+    q = rng_bf16(rng, (total, hq, d)) if dtype == oracle.BF16 else \
+        rng.standard_normal((total, hq, d)).astype(np.float32)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    return q, ks, vs, kp, vp, tab, qs
+
+
+def check_prefill_sdpa(prefill, dtype=oracle.BF16, hq=8, hkv=2):
+    """torch attention in fp64 on contiguous K/V with a lower-triangular mask
+    shifted by the prior context (torch.tril with diagonal L - n)."""
+    rng = np.random.default_rng(41)
+    ctx = [37, 1, 64, 50, 0, 17, 20]
+    qlens = [37, 1, 5, 50, 0, 3, 1]
+    d, bs = 16, 16
+    q, ks, vs, kp, vp, tab, qs = prefill_case(rng, ctx, qlens, hq, hkv, d, bs, dtype)
+    scale = np.float32(1 / math.sqrt(d))
+    got = prefill(q, kp, vp, tab, np.asarray(ctx, np.int32), qs, scale, dtype, bs)
+    for s, (L, n) in enumerate(zip(ctx, qlens)):
+        if n == 0:
+            continue
+        qq = torch.from_numpy(oracle.bits_to_f64(q[qs[s]:qs[s + 1]], dtype)).permute(1, 0, 2)
+        kk = torch.from_numpy(oracle.bits_to_f64(ks[s], dtype)).permute(1, 0, 2)
+        vv = torch.from_numpy(oracle.bits_to_f64(vs[s], dtype)).permute(1, 0, 2)
+        mask = torch.ones(n, L, dtype=torch.bool).tril(diagonal=L - n)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, kk, vv, attn_mask=mask, scale=float(scale), enable_gqa=True).permute(1, 0, 2)
+        assert np.max(np.abs(got[qs[s]:qs[s + 1]] - ref.numpy())) <= 1e-12, s
+
+
+def check_prefill_brute_force(prefill, dtype=oracle.FP32):
+    """Each query token equals the scalar-loop brute force of a decode over
+    the sequence cut after that token's position."""
+    rng = np.random.default_rng(43)
+    ctx, qlens = [6, 9, 3], [6, 4, 1]
+    hq, hkv, d, bs = 4, 2, 5, 4
+    q, ks, vs, kp, vp, tab, qs = prefill_case(rng, ctx, qlens, hq, hkv, d, bs, dtype)
+    scale = np.float32(0.41)
+    got = prefill(q, kp, vp, tab, np.asarray(ctx, np.int32), qs, scale, dtype, bs)
+    for s, (L, n) in enumerate(zip(ctx, qlens)):
+        for i in range(n):
+            t = qs[s] + i
+            ref = brute_force_decode(q[t][None], kp, vp, tab[s:s + 1], [L - n + i + 1], scale,
+                                     dtype, bs)
+            assert np.max(np.abs(got[t] - ref[0])) <= 1e-12, (s, i)
+
+
+def check_prefill_closed_forms(prefill, decode):
+    rng = np.random.default_rng(47)
+    hq = hkv = 2
+    d, bs = 8, 4
+    # A fresh prompt's first token sees only itself: out = v0 exactly.
+    ctx = qlens = [9, 1, 4]
+    q, ks, vs, kp, vp, tab, qs = prefill_case(rng, ctx, qlens, hq, hkv, d, bs, oracle.FP32)
+    out = prefill(q, kp, vp, tab, np.asarray(ctx, np.int32), qs, np.float32(0.3), oracle.FP32, bs)
+    for s in range(3):
+        assert np.array_equal(out[qs[s]], vs[s][0].astype(np.float64))
+    # q = 0: uniform weights over the visible positions -> running mean of V.
+    ctx, qlens = [11, 7], [11, 3]
+    q, ks, vs, kp, vp, tab, qs = prefill_case(rng, ctx, qlens, hq, hkv, d, bs, oracle.FP32)
+    q[:] = 0
+    out = prefill(q, kp, vp, tab, np.asarray(ctx, np.int32), qs, np.float32(0.3), oracle.FP32, bs)
+    for s, (L, n) in enumerate(zip(ctx, qlens)):
+        v = vs[s].astype(np.float64)
+        running = np.cumsum(v, axis=0) / np.arange(1, L + 1)[:, None, None]
+        for i in range(n):
+            assert np.max(np.abs(out[qs[s] + i] - running[L - n + i])) <= 1e-14
+    # One query token per sequence is a decode step.
+    ctx = [13, 5, 1]
+    q, ks, vs, kp, vp, tab, qs = prefill_case(rng, ctx, [1, 1, 1], 4, 2, d, bs, oracle.BF16)
+    a = prefill(q, kp, vp, tab, np.asarray(ctx, np.int32), qs, np.float32(0.3), oracle.BF16, bs)
+    b = decode(q, kp, vp, tab, np.asarray(ctx, np.int32), np.float32(0.3), oracle.BF16, bs)
+    assert np.array_equal(a, b)
+
+
+def check_prefill_chunking(prefill):
+    """A prompt processed as one chunk equals the same prompt processed as two
+    chunks (the first with only its own tokens cached)."""
+    rng = np.random.default_rng(53)
+    L, first = 23, 9
+    hq, hkv, d, bs = 4, 1, 8, 4
+    q, ks, vs, kp, vp, tab, qs = prefill_case(rng, [L], [L], hq, hkv, d, bs, oracle.BF16)
+    whole = prefill(q, kp, vp, tab, np.asarray([L], np.int32), qs, np.float32(0.35),
+                    oracle.BF16, bs)
+    a = prefill(q[:first], kp, vp, tab, np.asarray([first], np.int32),
+                np.asarray([0, first], np.int32), np.float32(0.35), oracle.BF16, bs)
+    b = prefill(q[first:], kp, vp, tab, np.asarray([L], np.int32),
+                np.asarray([0, L - first], np.int32), np.float32(0.35), oracle.BF16, bs)
+    assert np.array_equal(whole, np.concatenate([a, b]))
+
+
+def check_prefill_all(prefill, decode):
+    check_prefill_sdpa(prefill)
+    check_prefill_sdpa(prefill, oracle.FP32, hq=3, hkv=3)
+    check_prefill_brute_force(prefill)
+    check_prefill_closed_forms(prefill, decode)
+    check_prefill_chunking(prefill)
+
+
 # ------------------------------------------------------------------- the tests
 def test_bits_widening_matches_torch():
     check_bits(oracle.bits_to_f64)
@@ -394,6 +504,24 @@ def test_rows_subset_equals_full():
         assert np.array_equal(part[s, h], full[s, h])
 
 
+def test_prefill_matches_torch_sdpa_with_shifted_causal_mask():
+    check_prefill_sdpa(oracle.prefill)
+    check_prefill_sdpa(oracle.prefill, oracle.FP32, hq=3, hkv=3)
+
+
+def test_prefill_matches_brute_force():
+    check_prefill_brute_force(oracle.prefill)
+    check_prefill_brute_force(oracle.prefill, oracle.BF16)
+
+
+def test_prefill_closed_forms():
+    check_prefill_closed_forms(oracle.prefill, oracle.decode)
+
+
+def test_prefill_one_chunk_equals_two():
+    check_prefill_chunking(oracle.prefill)
+
+
 # ------------------------------------------------------- planted mistakes (CPU)
 def _mutants():
     """Plausible oracle bugs, each as (name, patches to oracle.paged_attention)."""
@@ -450,6 +578,33 @@ def test_planted_mistakes_are_caught(monkeypatch, name, patches):
         monkeypatch.setattr(pa, attr, fn)
     with pytest.raises((AssertionError, IndexError, ValueError)):
         check_decode_all(pa.decode)
+
+
+@pytest.mark.parametrize("name,patches", _mutants(), ids=[m[0] for m in _mutants()])
+def test_planted_mistakes_are_caught_by_prefill_pins(monkeypatch, name, patches):
+    for attr, fn in patches.items():
+        monkeypatch.setattr(pa, attr, fn)
+    with pytest.raises((AssertionError, IndexError, ValueError)):
+        check_prefill_all(pa.prefill, oracle.decode)
+
+
+def _prefill_mutants():
+    return [
+        ("self_excluded", {"visible_keys": lambda p: int(p)}),
+        ("one_ahead", {"visible_keys": lambda p: int(p) + 2}),
+        ("sees_whole_context", {"visible_keys": lambda p: 1 << 30}),
+        ("ignores_prior_context", {"query_position": lambda L, n, i: int(i)}),
+        ("chunk_from_the_front", {"query_position": lambda L, n, i: int(L) - int(n) + int(i) - 1
+                                  if int(i) > 0 else 0}),
+    ]
+
+
+@pytest.mark.parametrize("name,patches", _prefill_mutants(), ids=[m[0] for m in _prefill_mutants()])
+def test_planted_prefill_mistakes_are_caught(monkeypatch, name, patches):
+    for attr, fn in patches.items():
+        monkeypatch.setattr(pa, attr, fn)
+    with pytest.raises((AssertionError, IndexError, ValueError)):
+        check_prefill_all(pa.prefill, oracle.decode)
 
 
 def test_planted_append_and_copy_mistakes_are_caught(monkeypatch):
