@@ -6,6 +6,8 @@
  *   pa_copy_blocks  copy whole blocks (the copy in copy-on-write);
  *   pa_decode       one decode step of attention for every sequence, reading each
  *                   sequence's keys/values through its block table.
+ *   pa_prefill      attention of a multi-token query chunk per sequence (a prompt,
+ *                   or a piece of one) with a causal mask, through the block table;
  * and, for a model whose layers each own a pool, layer-batched forms of the
  * first two (pa_append_kv_layers, pa_copy_blocks_layers): one call serves
  * every layer.
@@ -169,6 +171,34 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
               const void* k_new, const void* v_new, const int64_t* slot_mapping,
               void* workspace, size_t workspace_bytes, int num_workers,
               int dtype, void* stream);
+
+/* Multi-token (prompt / chunked-prompt) paged attention.  Pages: catalogue
+ * note, method paragraph (attention reads through the block table) and
+ * "Block tables: logical order, physical scatter" (logical order = the
+ * sequence's order).  The query chunk of sequence s is its newest
+ * n_s = query_start[s+1] - query_start[s] tokens, whose keys/values are
+ * already in the pools (pa_append_kv / pa_append_kv_layers with their slots
+ * first); query token i of the chunk sits at position
+ * p = context_lens[s] - n_s + i and attends to positions 0..p (causal):
+ *   out[t,h] = sum_{j <= p} softmax_j(scale * q[t,h] . K_j) V_j,
+ *   t = query_start[s] + i, K_j/V_j of KV head h / (num_q_heads / num_kv_heads).
+ *   out, q         [num_query_tokens, num_q_heads, head_dim]   written / read
+ *   query_start    int32 [num_seqs + 1]: 0 = query_start[0] <= ... <=
+ *                  query_start[num_seqs] = num_query_tokens
+ *   context_lens   int32 [num_seqs]: tokens cached, chunk included
+ *   max_query_len  upper bound of every n_s (sizes the grid)
+ * A chunk of one token is a decode step.  Supported: bf16, head_dim 128,
+ * block_size 16 or 32 (else PA_ERR_UNSUPPORTED); fp32 accumulation, P
+ * rounded to bf16 for the P.V product.  Contract: n_s <= max_query_len,
+ * n_s <= context_lens[s] <= max_blocks_per_seq * block_size, table entries of
+ * used blocks in [0, num_blocks) -- checked under PA_CHECK=1.  No workspace.
+ * num_seqs == 0, max_query_len == 0 or num_query_tokens == 0 is a no-op. */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, int max_blocks_per_seq,
+               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+               int max_query_len, int64_t num_query_tokens, int num_q_heads, int num_kv_heads,
+               int head_dim, int block_size, int64_t num_blocks, float scale, int dtype,
+               void* stream);
 
 /* Measurement hook.  `before` and `after` are hipEvent_t handles (created by
  * the caller).  While set, every pa_decode call made from this host thread

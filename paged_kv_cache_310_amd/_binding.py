@@ -70,6 +70,9 @@ def _load():
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i64,
                                   ctypes.c_float, vp, vp, vp, vp, sz, i32, i32, vp]
         lib.pa_decode.restype = i32
+        lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i64, i32, i32, i32,
+                                   i32, i64, ctypes.c_float, i32, vp]
+        lib.pa_prefill.restype = i32
         lib.pa_set_decode_events.argtypes = [vp, vp]
         lib.pa_set_decode_events.restype = i32
         _lib = lib
@@ -267,4 +270,39 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
         _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(workspace),
         workspace.numel() * workspace.element_size(), int(num_workers), _dtype_code(q),
         _stream(q.device, stream)))
+    return out
+
+
+def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+               max_query_len: Optional[int] = None, out=None, stream=None) -> torch.Tensor:
+    """Causal attention of each sequence's query chunk (its newest tokens,
+    already appended) through the block table; returns ``out``
+    [num_query_tokens, num_q_heads, head_dim].  ``max_query_len`` bounds every
+    chunk; when omitted it is read from ``query_start`` (a device-to-host
+    copy)."""
+    nb, hkv, bs, d = _check_cache(k_cache, v_cache)
+    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == k_cache.dtype and q.is_contiguous()
+          and q.device == k_cache.device,
+          "q must be [num_query_tokens, num_q_heads, head_dim] like the pools")
+    t, hq, _ = q.shape
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.is_contiguous() and block_tables.device == q.device,
+          "block_tables must be int32 [num_seqs, max_blocks]")
+    b = block_tables.shape[0]
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (b,)
+          and context_lens.is_contiguous() and context_lens.device == q.device,
+          "context_lens must be int32 [num_seqs]")
+    _need(query_start.dtype == torch.int32 and query_start.shape == (b + 1,)
+          and query_start.is_contiguous() and query_start.device == q.device,
+          "query_start must be int32 [num_seqs + 1]")
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if b else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
+          and out.device == q.device, "out must match q")
+    _call("pa_prefill", _load().pa_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), _ptr(query_start), b, int(max_query_len), t,
+        hq, hkv, d, bs, nb, float(scale), _dtype_code(q), _stream(q.device, stream)))
     return out

@@ -1,4 +1,4 @@
-// Device helpers shared by the decode kernels of libpa.so (gfx950).
+// Device helpers shared by the attention kernels of libpa.so (gfx950).
 #pragma once
 
 #include "pa_internal.h"
@@ -20,6 +20,27 @@ typedef const int32_t __attribute__((address_space(4))) const_i32;
 typedef const int64_t __attribute__((address_space(4))) const_i64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t __attribute__((address_space(3))) lds_i32;
+
+// Operand and accumulator types of the 16x16 MFMA instructions.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// A 16x16 MFMA result leaves column n of the output in the four lanes with
+// l%16 == n (one per lane group l/16).
+// Sum (or max) of a value over the four lanes that share l%16.
+__device__ __forceinline__ float group4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float group4_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // Buffer resource for one tile: scalar 48-bit base, byte range [0, bytes).
 // Loads through it take a 32-bit per-lane offset and return 0 outside the range.

@@ -37,10 +37,6 @@ namespace {
 
 using namespace dev;
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kD = 128;
 constexpr int kRow = kD * 2;                 // bytes of one token row (bf16)
 constexpr int kTile = kChunk * kRow;         // 4 KiB
@@ -48,19 +44,6 @@ constexpr int kTile = kChunk * kRow;         // 4 KiB
 // Token (within the chunk) of MFMA row / k-index m.
 __device__ __forceinline__ int token_of(int m) { return 4 * (m & 3) + (m >> 2); }
 
-// Sum (or max) of a value over the four lanes that share l%16.
-__device__ __forceinline__ float group4_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ __forceinline__ float group4_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
   const uint32_t d = v[e >> 1];

@@ -351,4 +351,67 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
              : PA_ERR_HIP;
 }
 
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, int max_blocks_per_seq,
+               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+               int max_query_len, int64_t num_query_tokens, int num_q_heads, int num_kv_heads,
+               int head_dim, int block_size, int64_t num_blocks, float scale, int dtype,
+               void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_query_len < 0 || num_query_tokens < 0 ||
+      num_q_heads <= 0 || !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks) ||
+      num_q_heads % num_kv_heads != 0 || !(scale == scale))
+    return PA_ERR_INVALID;
+  const int sup = support_status(dtype, block_size, head_dim);
+  if (sup != PA_OK) return sup;
+  if (!pa::prefill_supported(dtype, head_dim, block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_query_len == 0 || num_query_tokens == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_INVALID;
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t tiles =
+      ((int64_t)max_query_len * group + pa::kPrefillRowsPerWg - 1) / pa::kPrefillRowsPerWg;
+  if (tiles * num_seqs * num_kv_heads > INT32_MAX || num_query_tokens * num_q_heads > INT32_MAX)
+    return PA_ERR_UNSUPPORTED;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    std::vector<int32_t> lens, starts, tables;
+    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, st)) return PA_ERR_HIP;
+    if (!copy_to_host(starts, query_start, (size_t)num_seqs + 1, st)) return PA_ERR_HIP;
+    if (!copy_to_host(tables, block_tables, (size_t)num_seqs * max_blocks_per_seq, st))
+      return PA_ERR_HIP;
+    if (starts[0] != 0 || starts[(size_t)num_seqs] != num_query_tokens) return PA_ERR_INDEX;
+    for (int s = 0; s < num_seqs; ++s) {
+      const int64_t L = lens[(size_t)s];
+      const int64_t nq = (int64_t)starts[(size_t)s + 1] - starts[(size_t)s];
+      if (nq < 0 || nq > max_query_len || nq > L) return PA_ERR_INDEX;
+      if (L > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_INDEX;
+      const int64_t nblk = (L + block_size - 1) / block_size;
+      for (int64_t j = 0; j < nblk; ++j) {
+        const int64_t b = tables[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= num_blocks) return PA_ERR_INDEX;
+      }
+    }
+  }
+
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.tiles_per_seq = (int)tiles;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return pa::launch_prefill(a, block_size, st) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // extern "C"

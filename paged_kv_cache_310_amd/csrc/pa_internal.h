@@ -91,6 +91,29 @@ hipError_t decode_resident_per_cu(int dtype, int head_dim, int block_size, int g
 bool gqa_supported(int dtype, int head_dim, int group);
 hipError_t launch_gqa_attention(const DecodeArgs& a, int block_size, int workers,
                                 hipStream_t stream, int* resident);
+// Multi-token (prefill) attention: what the kernel reads, by value.
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;   // [num_seqs + 1]
+  int64_t max_blocks_per_seq;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                    // num_q_heads / num_kv_heads
+  int tiles_per_seq;            // row tiles per (sequence, KV head)
+  float scale_log2;             // scale * log2(e)
+};
+// Query rows (query token x query head of one KV head) per prefill workgroup.
+constexpr int kPrefillRowsPerWg = 128;
+// bf16, head_dim 128, block_size 16 or 32.
+bool prefill_supported(int dtype, int head_dim, int block_size);
+hipError_t launch_prefill(const PrefillArgs& a, int block_size, hipStream_t stream);
+
 // Layers served by one multi-layer append or copy launch (their pool
 // pointers travel in the kernel arguments).
 constexpr int kMaxLayersPerLaunch = 32;

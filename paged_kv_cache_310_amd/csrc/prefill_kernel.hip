@@ -1,0 +1,281 @@
+// Multi-token (prompt / chunked-prompt) paged attention on the gfx950 matrix
+// cores: bf16, head_dim 128, block size 16 or 32.
+//
+// What is computed (pages on "Efficient Memory Management for Large Language
+// Model Serving with PagedAttention": catalogue note, method paragraph --
+// attention reads keys and values through the block table; zeroshotmind.com
+// essay, "Block tables: logical order, physical scatter"): the query chunk of
+// a sequence is its newest tokens, already appended to the pool; query token
+// i of an n-token chunk sits at position L - n + i of the L cached tokens and
+// attends to positions 0..L - n + i, gathered through the sequence's table.
+//
+// Work: one workgroup (4 waves) per 128 query rows of one (sequence, KV
+// head).  A row is a (query token, query head) pair of the KV head's group,
+// token-major, so grouped query heads share every K/V tile.  Each wave owns
+// 32 rows as two 16-row MFMA tiles.  The workgroup walks the keys in steps of
+// 32 (two 16-token halves): all 256 threads load the step's K and V rows
+// through the table into registers one step ahead, and store them to one of
+// two LDS buffers, so the global loads of step t+1 overlap the products of
+// step t and one barrier per step suffices.
+//
+// Per step and 16-row tile (lane l, lane group g = l/16, column n = l%16):
+//  * S^T[16 keys x 16 rows] = K . Q^T for each 16-key half, four
+//    v_mfma_f32_16x16x32_bf16 over the 128 dims.  K (A operand) is read from
+//    LDS, Q^T (B operand) stays in registers for the whole key walk.  Lane l
+//    receives the scores of keys 4g+i (i = 0..3) of the half for row n.
+//  * Causal mask (key position > row position -> -inf), online softmax in
+//    the exp2 domain; the row's running max is agreed on by the four lanes
+//    holding column n (two permlane swaps).  P is rounded to bf16 for the
+//    product, and the running sum adds the same rounded values.
+//  * O^T[128 dims x 16 rows] += V^T . P^T, eight v_mfma_f32_16x16x32_bf16
+//    (one per c = 0..7).  The 32 keys of the k-dimension are ordered so that
+//    lane l's eight P values are exactly its B operand: k = 8g+i is key 4g+i
+//    and k = 8g+4+i is key 16+4g+i.  The A operand of MFMA c is element c of
+//    eight 16-byte LDS reads of V (lane l: those eight keys, dims 8n..8n+7),
+//    so MFMA c produces dims 8m + c and lane l ends up holding the 32
+//    contiguous dims 32g..32g+31 of row n.
+#include "decode_common.h"
+
+namespace pa {
+namespace {
+
+using namespace dev;
+
+constexpr int kPD = 128;                      // head_dim
+constexpr int kPRow = kPD * 2;                // bytes of one token row
+constexpr int kKeys = 32;                     // keys per step
+constexpr int kWaves = 4;
+constexpr int kRowTiles = 2;                  // 16-row MFMA tiles per wave
+constexpr int kRowsPerWave = 16 * kRowTiles;
+static_assert(kWaves * kRowsPerWave == kPrefillRowsPerWg, "rows per workgroup");
+// K rows are padded by 16 bytes in LDS: the 16 rows one A-operand read
+// touches then start on 16 different 4-bank groups.
+constexpr int kKStride = kPRow + 16;
+constexpr int kKBytes = kKeys * kKStride;
+constexpr int kVBytes = kKeys * kPRow;
+constexpr int kBufBytes = kKBytes + kVBytes;
+
+typedef uint32_t __attribute__((address_space(3))) lds_u32;
+
+__device__ __forceinline__ u32x4 lds_load16(const char* base, int offset) {
+  return *reinterpret_cast<const u32x4*>(base + offset);
+}
+__device__ __forceinline__ void lds_store16(char* base, int offset, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(base + offset) = v;
+}
+
+// bf16 element e of a 16-byte row fragment, as the low 16 bits.
+__device__ __forceinline__ uint32_t elem16(const u32x4& v, int e) {
+  const uint32_t d = v[e >> 1];
+  return (e & 1) ? (d >> 16) : (d & 0xFFFFu);
+}
+
+template <int BS>
+__global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2][kBufBytes];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g4 = lane >> 4;
+  const int n = lane & 15;
+  const int HKV = a.num_kv_heads;
+  const int HQ = a.num_q_heads;
+  const int G = a.group;
+
+  // The last row tiles of every (sequence, KV head) see the most keys under
+  // the causal mask: they are dispatched first.
+  const int pairs = a.num_seqs * HKV;
+  const int tile = a.tiles_per_seq - 1 - (int)blockIdx.x / pairs;
+  const int pair = (int)blockIdx.x % pairs;
+  const int s = pair / HKV;
+  const int hk = pair % HKV;
+  const int q0 = a.query_start[s];
+  const int nq = a.query_start[s + 1] - q0;
+  const int L = a.context_lens[s];
+  const int rows = nq * G;
+  const int row0 = tile * kPrefillRowsPerWg;
+  if (row0 >= rows) return;                       // the whole workgroup leaves
+  const int last_row = min(row0 + kPrefillRowsPerWg, rows) - 1;
+  const int p_max = L - nq + last_row / G;       // highest position a row here has
+  const int steps = p_max / kKeys + 1;
+
+  const int wrow0 = row0 + wave * kRowsPerWave;
+  const bool wave_rows = wrow0 < rows;
+  const int wave_pmax = wave_rows ? L - nq + (min(wrow0 + kRowsPerWave, rows) - 1) / G : -1;
+
+  // This lane's row of each tile: position and Q^T operand (dims 32c+8g..+8).
+  int pos[kRowTiles];
+  u32x4 qop[kRowTiles][4];
+  const char* qbase = static_cast<const char*>(a.q);
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    const int r = wrow0 + 16 * rt + n;
+    const bool real = r < rows;
+    const int token = real ? r / G : 0;
+    const int head = hk * G + (real ? r % G : 0);
+    pos[rt] = real ? L - nq + token : p_max;
+    const char* row = qbase + ((int64_t)(q0 + token) * HQ + head) * kPRow + g4 * 16;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qop[rt][c] = real ? *reinterpret_cast<const u32x4*>(row + c * 64) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Step loads: thread tid moves key (tid/16) + 16h of the step, 16 bytes
+  // (dims 8*(tid%16)..+8), for h = 0, 1; keys at or past L load zeros.
+  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+  const int key_in_step = tid >> 4;
+  const int chunk = (tid & 15) * 16;
+  u32x4 kr[2], vr[2];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = k0 + key_in_step + 16 * h;
+      if (kk < L) {
+        const int64_t blk = table[kk / BS];
+        const int64_t off = (((blk * HKV + hk) * BS) + (kk % BS)) * kPRow + chunk;
+        kr[h] = *reinterpret_cast<const u32x4*>(kc + off);
+        vr[h] = *reinterpret_cast<const u32x4*>(vc + off);
+      } else {
+        kr[h] = u32x4{0u, 0u, 0u, 0u};
+        vr[h] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = key_in_step + 16 * h;
+      lds_store16(lds[buf], key * kKStride + chunk, kr[h]);
+      lds_store16(lds[buf] + kKBytes, key * kPRow + chunk, vr[h]);
+    }
+  };
+
+  f32x4_t acc[kRowTiles][8];
+  float m_run[kRowTiles], l_run[kRowTiles];
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int t = 0; t < steps; ++t) {
+    const int k0 = t * kKeys;
+    if (t + 1 < steps) fetch(k0 + kKeys);
+    if (wave_rows && k0 <= wave_pmax) {
+      const char* kb = lds[t & 1];
+      const char* vb = kb + kKBytes;
+      // A operands of K . Q^T: key 16*half + n, dims 32c + 8g..+8.
+      u32x4 kop[2][4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          kop[half][c] = lds_load16(kb, (16 * half + n) * kKStride + c * 64 + g4 * 16);
+      // V rows of this lane's eight keys (k = 8g..8g+7), dims 8n..8n+7.
+      u32x4 vrow[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = (j < 4) ? 4 * g4 + j : 16 + 4 * g4 + (j - 4);
+        vrow[j] = lds_load16(vb, key * kPRow + n * 16);
+      }
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) {
+        f32x4_t sc[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          sc[half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, kop[half][c]),
+                __builtin_bit_cast(bf16x8_t, qop[rt][c]), sc[half], 0, 0, 0);
+        }
+        // Scores in the exp2 domain, masked past the row's position.
+        float x[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 16 * half + 4 * g4 + i;
+            const float v = key <= pos[rt] ? sc[half][i] * a.scale_log2 : -INFINITY;
+            x[4 * half + i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = group4_max(mx);
+        const float m_new = fmaxf(m_run[rt], mx);
+        const float alpha = fast_exp2(m_run[rt] - m_new);
+        m_run[rt] = m_new;
+        uint32_t pb[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = f32_to_bf16(fast_exp2(x[2 * j] - m_new));
+          const uint32_t hi = f32_to_bf16(fast_exp2(x[2 * j + 1] - m_new));
+          psum += bf_lo(lo) + bf_lo(hi);
+          pb[j] = lo | (hi << 16);
+        }
+        l_run[rt] = fmaf(l_run[rt], alpha, psum);
+        const u32x4 pop = u32x4{pb[0], pb[1], pb[2], pb[3]};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          acc[rt][c] *= alpha;
+          const u32x4 va = u32x4{elem16(vrow[0], c) | (elem16(vrow[1], c) << 16),
+                                 elem16(vrow[2], c) | (elem16(vrow[3], c) << 16),
+                                 elem16(vrow[4], c) | (elem16(vrow[5], c) << 16),
+                                 elem16(vrow[6], c) | (elem16(vrow[7], c) << 16)};
+          acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pop), acc[rt][c],
+              0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < steps) stash((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // Normalise and store: lane l holds dims 32g + 8i + c (c = 0..7) of its row.
+  char* obase = static_cast<char*>(a.out);
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    const float total = group4_sum(l_run[rt]);
+    const int r = wrow0 + 16 * rt + n;
+    if (r >= rows) continue;
+    const float inv = 1.f / total;
+    char* row = obase + ((int64_t)(q0 + r / G) * HQ + hk * G + r % G) * kPRow + g4 * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = f32_to_bf16(acc[rt][2 * j][i] * inv) | (f32_to_bf16(acc[rt][2 * j + 1][i] * inv) << 16);
+      *reinterpret_cast<u32x4*>(row + i * 16) = v;
+    }
+  }
+}
+
+}  // namespace
+
+bool prefill_supported(int dtype, int head_dim, int block_size) {
+  return dtype == kBf16 && head_dim == kPD && (block_size == 16 || block_size == 32);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int block_size, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.tiles_per_seq * a.num_seqs * a.num_kv_heads;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (block_size == 16)
+    hipLaunchKernelGGL(prefill_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

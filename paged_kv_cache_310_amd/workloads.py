@@ -312,3 +312,119 @@ def workload_lengths(name: str) -> np.ndarray:
     if name in ("gqa_pareto_bs16", "gqa_pareto_bs32"):
         return _pareto_lengths(np.random.default_rng(3105), 256)
     raise KeyError(name)
+
+
+# --------------------------------------------------------- multi-token queries
+@dataclass
+class PrefillWorkload:
+    """Inputs of one multi-token (prompt / chunked prompt) attention call.
+
+    Sequence ``s`` holds ``context_lens[s]`` tokens; its newest
+    ``n_s = query_start[s+1] - query_start[s]`` tokens are the query chunk.
+    ``k_new``/``v_new`` are the chunk's rows and ``slot_mapping`` their slots
+    (append them first); with ``poison=True`` those slots, and every slot no
+    sequence holds, are NaN in the pools until the append fills them.
+    """
+    name: str
+    dtype: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: np.float32
+    q: np.ndarray                 # [num_query_tokens, num_q_heads, head_dim]
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_tables: np.ndarray      # int32 [num_seqs, max_blocks]
+    context_lens: np.ndarray      # int32 [num_seqs]
+    query_start: np.ndarray       # int32 [num_seqs + 1]
+    k_new: np.ndarray             # [num_query_tokens, num_kv_heads, head_dim]
+    v_new: np.ndarray
+    slot_mapping: np.ndarray      # int64 [num_query_tokens]
+
+    @property
+    def num_query_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start.astype(np.int64))
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.num_seqs else 0
+
+
+def make_prefill(name: str, seed: int, dtype: str, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, block_size: int, context_lens, query_lens, poison: bool = True,
+                 rng: Optional[np.random.Generator] = None) -> PrefillWorkload:
+    """Sequences of ``context_lens`` tokens whose newest ``query_lens`` tokens
+    form the query chunk, blocks scattered over a pool 1.25x the need.
+
+    Draw order: pool permutation, q, K pool, V pool, new K, new V."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    nq = np.asarray(query_lens, dtype=np.int64)
+    if ctx.shape != nq.shape or np.any(nq < 0) or np.any(nq > ctx):
+        raise ValueError("need 0 <= query_lens <= context_lens, one per sequence")
+    b, bs = len(ctx), block_size
+    per_seq = [blocks_needed(int(n), bs) for n in ctx]
+    num_blocks = max(_pool_size(sum(per_seq)), 1)
+    perm = rng.permutation(num_blocks)
+    tables = np.full((b, max(max(per_seq, default=1), 1)), -1, dtype=np.int32)
+    used = 0
+    for s, k in enumerate(per_seq):
+        tables[s, :k] = perm[used:used + k]
+        used += k
+    starts = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    total = int(starts[-1])
+    q = normal_bits(rng, (total, num_q_heads, head_dim), dtype)
+    k_cache = normal_bits(rng, (num_blocks, num_kv_heads, bs, head_dim), dtype)
+    v_cache = normal_bits(rng, (num_blocks, num_kv_heads, bs, head_dim), dtype)
+    k_new = normal_bits(rng, (total, num_kv_heads, head_dim), dtype)
+    v_new = normal_bits(rng, (total, num_kv_heads, head_dim), dtype)
+    slots = np.empty(total, dtype=np.int64)
+    held = np.zeros((num_blocks, bs), dtype=bool)      # slots holding an earlier token
+    for s in range(b):
+        L, n = int(ctx[s]), int(nq[s])
+        for p in range(L):
+            blk, off = int(tables[s, p // bs]), p % bs
+            if p < L - n:
+                held[blk, off] = True
+            else:
+                slots[starts[s] + p - (L - n)] = blk * bs + off
+    if poison:
+        blk, off = np.nonzero(~held)
+        k_cache[blk, :, off, :] = nan_bits(dtype)
+        v_cache[blk, :, off, :] = nan_bits(dtype)
+    return PrefillWorkload(name, dtype, b, num_q_heads, num_kv_heads, head_dim, bs, num_blocks,
+                           np.float32(1.0 / math.sqrt(head_dim)), q, k_cache, v_cache, tables,
+                           ctx.astype(np.int32), starts, k_new, v_new, slots)
+
+
+PREFILL_WORKLOADS = ("llama13b_prefill", "gqa_chunked_prefill")
+
+
+def make_prefill_workload(name: str, poison: bool = True) -> PrefillWorkload:
+    """Named multi-token workloads (the pages give no prompt workload; these
+    keep the decode workloads' head shapes and block size):
+
+    * llama13b_prefill: 8 fresh prompts, lengths U[512, 2048], 40/40 heads,
+      d 128, bs 16, bf16 -- the whole prompt is the chunk;
+    * gqa_chunked_prefill: 16 sequences, 64 query heads over 8 KV heads, d 128,
+      bs 16, bf16, a 512-token chunk on top of an earlier context of
+      lognormal(median 2048, sigma ln 2) tokens clipped to [256, 8192].
+    """
+    if name == "llama13b_prefill":
+        rng = np.random.default_rng(3110)
+        lens = rng.integers(512, 2049, 8)
+        return make_prefill(name, 3110, BF16, 40, 40, 128, 16, lens, lens, poison, rng)
+    if name == "gqa_chunked_prefill":
+        rng = np.random.default_rng(3111)
+        prior = np.clip(np.rint(rng.lognormal(math.log(2048), math.log(2), 16)), 256, 8192)
+        prior = prior.astype(np.int64)
+        return make_prefill(name, 3111, BF16, 64, 8, 128, 16, prior + 512,
+                            np.full(16, 512), poison, rng)
+    raise KeyError(f"unknown prefill workload {name!r}; choose from {PREFILL_WORKLOADS}")

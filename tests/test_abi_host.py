@@ -130,6 +130,33 @@ def test_layer_batched_calls_reject_bad_arguments(lib):
     assert cp(three, three, 3, None, 4, 10, 8, 16, 128, 1, None) == 1
 
 
+def prefill_status(lib, **kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tab=FAKE, mb=4, lens=FAKE, qs=FAKE, b=2, mq=8,
+                t=10, hq=8, hkv=2, d=128, bs=16, nb=10, scale=0.1, dtype=1)
+    args.update(kw)
+    return lib.pa_prefill(args["out"], args["q"], args["k"], args["v"], args["tab"], args["mb"],
+                          args["lens"], args["qs"], args["b"], args["mq"], args["t"], args["hq"],
+                          args["hkv"], args["d"], args["bs"], args["nb"], args["scale"],
+                          args["dtype"], None)
+
+
+def test_prefill_rejects_bad_arguments_before_any_hip_call(lib):
+    assert prefill_status(lib, dtype=0) == 2              # fp32: no prefill kernel
+    assert prefill_status(lib, d=64) == 2
+    assert prefill_status(lib, bs=8) == 2
+    assert prefill_status(lib, hq=6, hkv=4) == 1
+    assert prefill_status(lib, b=-1) == 1
+    assert prefill_status(lib, mq=-1) == 1
+    assert prefill_status(lib, t=-1) == 1
+    assert prefill_status(lib, mb=0) == 1
+    assert prefill_status(lib, scale=float("nan")) == 1
+    assert prefill_status(lib, qs=None) == 1
+    assert prefill_status(lib, out=FAKE + 2) == 1         # not 16-byte aligned
+    assert prefill_status(lib, b=0) == 0                  # nothing to do
+    assert prefill_status(lib, mq=0) == 0
+    assert prefill_status(lib, t=0) == 0
+
+
 def test_decode_event_hook_arguments(lib):
     assert lib.pa_set_decode_events(FAKE, None) == 1
     assert lib.pa_set_decode_events(None, FAKE) == 1
