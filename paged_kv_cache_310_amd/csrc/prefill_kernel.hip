@@ -16,7 +16,9 @@
 // 32 (two 16-token halves): all 256 threads load the step's K and V rows
 // through the table into registers one step ahead, and store them to one of
 // two LDS buffers, so the global loads of step t+1 overlap the products of
-// step t and one barrier per step suffices.
+// step t and one barrier per step suffices.  The sequence's block-table
+// entries are staged in LDS (kTableCap at a time), so no step waits on a
+// table read before it can address its K/V rows.
 //
 // Per step and 16-row tile (lane l, lane group g = l/16, column n = l%16):
 //  * S^T[16 keys x 16 rows] = K . Q^T for each 16-key half, four
@@ -24,9 +26,14 @@
 //    LDS, Q^T (B operand) stays in registers for the whole key walk.  Lane l
 //    receives the scores of keys 4g+i (i = 0..3) of the half for row n.
 //  * Causal mask (key position > row position -> -inf), online softmax in
-//    the exp2 domain; the row's running max is agreed on by the four lanes
-//    holding column n (two permlane swaps).  P is rounded to bf16 for the
-//    product, and the running sum adds the same rounded values.
+//    the exp2 domain; the row's tile max is agreed on by the four lanes
+//    holding column n (two permlane swaps).  The reference max a row's
+//    weights are taken against moves only when the tile max exceeds it by
+//    more than kRescaleSlack (so weights stay below 2^kRescaleSlack), and
+//    the accumulators are rescaled only in a step where some row's moved:
+//    after the first steps that is rare, and the result (acc / sum) does not
+//    depend on the reference.  P is rounded to bf16 for the product, and the
+//    running sum adds the same rounded values.
 //  * O^T[128 dims x 16 rows] += V^T . P^T, eight v_mfma_f32_16x16x32_bf16
 //    (one per c = 0..7).  The 32 keys of the k-dimension are ordered so that
 //    lane l's eight P values are exactly its B operand: k = 8g+i is key 4g+i
@@ -54,6 +61,11 @@ constexpr int kKStride = kPRow + 16;
 constexpr int kKBytes = kKeys * kKStride;
 constexpr int kVBytes = kKeys * kPRow;
 constexpr int kBufBytes = kKBytes + kVBytes;
+// Block-table entries held in LDS at a time (refilled every
+// kTableCap * BS / kKeys steps).
+constexpr int kTableCap = 1024;
+// log2 of the largest weight the lazy rescale lets through.
+constexpr float kRescaleSlack = 8.f;
 
 typedef uint32_t __attribute__((address_space(3))) lds_u32;
 
@@ -64,15 +76,22 @@ __device__ __forceinline__ void lds_store16(char* base, int offset, const u32x4&
   *reinterpret_cast<u32x4*>(base + offset) = v;
 }
 
-// bf16 element e of a 16-byte row fragment, as the low 16 bits.
-__device__ __forceinline__ uint32_t elem16(const u32x4& v, int e) {
-  const uint32_t d = v[e >> 1];
-  return (e & 1) ? (d >> 16) : (d & 0xFFFFu);
+// Element e (bf16) of fragment a in the low half, of fragment b in the high
+// half: one v_perm_b32.
+__device__ __forceinline__ uint32_t pair16(const u32x4& a, const u32x4& b, int e) {
+  return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two floats to two bf16 (round to nearest even), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 template <int BS>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][kBufBytes];
+  __shared__ int32_t tab[kTableCap];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -120,9 +139,20 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs a) {
       qop[rt][c] = real ? *reinterpret_cast<const u32x4*>(row + c * 64) : u32x4{0u, 0u, 0u, 0u};
   }
 
+  // Block-table entries [first, first + kTableCap) of the blocks the keys up
+  // to p_max use, staged in LDS.
+  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int used_blocks = min(L, p_max + kKeys) / BS + 1;   // bound; only entries < ceil(L/BS) are read
+  const int table_len = min(used_blocks, (L + BS - 1) / BS);
+  auto stage_table = [&](int first) {
+    for (int i = tid; i < kTableCap && first + i < table_len; i += 256) tab[i] = table[first + i];
+  };
+  constexpr int kStepsPerTable = kTableCap * BS / kKeys;
+  stage_table(0);
+  __syncthreads();
+
   // Step loads: thread tid moves key (tid/16) + 16h of the step, 16 bytes
   // (dims 8*(tid%16)..+8), for h = 0, 1; keys at or past L load zeros.
-  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
   const int key_in_step = tid >> 4;
@@ -133,7 +163,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs a) {
     for (int h = 0; h < 2; ++h) {
       const int kk = k0 + key_in_step + 16 * h;
       if (kk < L) {
-        const int64_t blk = table[kk / BS];
+        const int64_t blk = tab[(kk / BS) % kTableCap];
         const int64_t off = (((blk * HKV + hk) * BS) + (kk % BS)) * kPRow + chunk;
         kr[h] = *reinterpret_cast<const u32x4*>(kc + off);
         vr[h] = *reinterpret_cast<const u32x4*>(vc + off);
@@ -167,6 +197,14 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs a) {
   __syncthreads();
   for (int t = 0; t < steps; ++t) {
     const int k0 = t * kKeys;
+    if (t + 1 < steps && (t + 1) % kStepsPerTable == 0) {
+      // The next step's keys need the next table window: every thread has
+      // finished reading the current one (its last fetch was the previous
+      // step's), so refill it between two barriers.
+      __syncthreads();
+      stage_table((t + 1) / kStepsPerTable * kTableCap);
+      __syncthreads();
+    }
     if (t + 1 < steps) fetch(k0 + kKeys);
     if (wave_rows && k0 <= wave_pmax) {
       const char* kb = lds[t & 1];
@@ -185,6 +223,12 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs a) {
         const int key = (j < 4) ? 4 * g4 + j : 16 + 4 * g4 + (j - 4);
         vrow[j] = lds_load16(vb, key * kPRow + n * 16);
       }
+      // A operands of V^T . P^T: element c of the eight rows (dim 8n + c).
+      u32x4 va[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        va[c] = u32x4{pair16(vrow[0], vrow[1], c), pair16(vrow[2], vrow[3], c),
+                      pair16(vrow[4], vrow[5], c), pair16(vrow[6], vrow[7], c)};
 #pragma unroll
       for (int rt = 0; rt < kRowTiles; ++rt) {
         f32x4_t sc[2];
@@ -210,31 +254,29 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs a) {
             mx = fmaxf(mx, v);
           }
         mx = group4_max(mx);
-        const float m_new = fmaxf(m_run[rt], mx);
-        const float alpha = fast_exp2(m_run[rt] - m_new);
-        m_run[rt] = m_new;
+        const bool grow = mx > m_run[rt] + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? mx : m_run[rt];
+          const float alpha = fast_exp2(m_run[rt] - m_new);   // 1 where the reference stays
+          m_run[rt] = m_new;
+          l_run[rt] *= alpha;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[rt][c] *= alpha;
+        }
         uint32_t pb[4];
         float psum = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = f32_to_bf16(fast_exp2(x[2 * j] - m_new));
-          const uint32_t hi = f32_to_bf16(fast_exp2(x[2 * j + 1] - m_new));
-          psum += bf_lo(lo) + bf_lo(hi);
-          pb[j] = lo | (hi << 16);
+          pb[j] = cvt_bf16x2(fast_exp2(x[2 * j] - m_run[rt]), fast_exp2(x[2 * j + 1] - m_run[rt]));
+          psum += bf_lo(pb[j]) + bf_hi(pb[j]);
         }
-        l_run[rt] = fmaf(l_run[rt], alpha, psum);
+        l_run[rt] += psum;
         const u32x4 pop = u32x4{pb[0], pb[1], pb[2], pb[3]};
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          acc[rt][c] *= alpha;
-          const u32x4 va = u32x4{elem16(vrow[0], c) | (elem16(vrow[1], c) << 16),
-                                 elem16(vrow[2], c) | (elem16(vrow[3], c) << 16),
-                                 elem16(vrow[4], c) | (elem16(vrow[5], c) << 16),
-                                 elem16(vrow[6], c) | (elem16(vrow[7], c) << 16)};
+        for (int c = 0; c < 8; ++c)
           acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pop), acc[rt][c],
+              __builtin_bit_cast(bf16x8_t, va[c]), __builtin_bit_cast(bf16x8_t, pop), acc[rt][c],
               0, 0, 0);
-        }
       }
     }
     if (t + 1 < steps) stash((t + 1) & 1);
@@ -255,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs a) {
       u32x4 v;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        v[j] = f32_to_bf16(acc[rt][2 * j][i] * inv) | (f32_to_bf16(acc[rt][2 * j + 1][i] * inv) << 16);
+        v[j] = cvt_bf16x2(acc[rt][2 * j][i] * inv, acc[rt][2 * j + 1][i] * inv);
       *reinterpret_cast<u32x4*>(row + i * 16) = v;
     }
   }

@@ -64,6 +64,19 @@ def test_small_ragged(hq, hkv, bs):
     say("max-abs %.3e row-rel %.3e" % err)
 
 
+@pytest.mark.parametrize("bs", [16, 32])
+def test_long_context_crosses_table_windows(bs):
+    """Contexts past 1024 table entries: the kernel restages its LDS copy of
+    the block table while walking the keys."""
+    say("prefill long", bs)
+    w = wl.make_prefill("long", 620 + bs, wl.BF16, 4, 2, 128, bs, [40000, 20000, 33000],
+                        [64, 1, 5])
+    got = out_f64(run_device(w))
+    ref = oracle_rows(w)
+    err = assert_attention_close(got, ref, wl.BF16)
+    say("max-abs %.3e row-rel %.3e" % err)
+
+
 def test_max_query_len_larger_than_needed_changes_nothing():
     w = wl.make_prefill("slack", 611, wl.BF16, 8, 2, 128, 16, [90, 40, 7], [90, 12, 7])
     a = run_device(w)
