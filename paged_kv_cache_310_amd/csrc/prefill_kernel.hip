@@ -9,14 +9,15 @@
 // i of an n-token chunk sits at position L - n + i of the L cached tokens and
 // attends to positions 0..L - n + i, gathered through the sequence's table.
 //
-// Work: one workgroup (4 waves) per 128 query rows of one (sequence, KV
+// Work: one workgroup (kWaves waves) per kWaves * 32 query rows of one (sequence, KV
 // head).  A row is a (query token, query head) pair of the KV head's group,
 // token-major, so grouped query heads share every K/V tile.  Each wave owns
 // 32 rows as two 16-row MFMA tiles.  The workgroup walks the keys in steps of
-// 32 (two 16-token halves): all 256 threads load the step's K and V rows
-// through the table into registers one step ahead, and store them to one of
-// two LDS buffers, so the global loads of step t+1 overlap the products of
-// step t and one barrier per step suffices.  The sequence's block-table
+// 32 (two 16-token halves): all threads load a step's K and V rows through
+// the table into registers kDepth steps ahead and store them to one of
+// kDepth + 1 LDS buffers after the step before it is computed, so the global
+// loads of the next steps overlap the products of this one and one barrier
+// per step suffices.  The sequence's block-table
 // entries are staged in LDS (kTableCap at a time), so no step waits on a
 // table read before it can address its K/V rows.
 //
@@ -26,14 +27,16 @@
 //    LDS, Q^T (B operand) stays in registers for the whole key walk.  Lane l
 //    receives the scores of keys 4g+i (i = 0..3) of the half for row n.
 //  * Causal mask (key position > row position -> -inf), online softmax in
-//    the exp2 domain; the row's tile max is agreed on by the four lanes
-//    holding column n (two permlane swaps).  The reference max a row's
+//    the exp2 domain (the scale is applied in the exponent's fma); the mask
+//    is evaluated only on steps that reach past the wave's lowest row
+//    position.  The row's tile max is agreed on by the four lanes holding
+//    column n (two permlane swaps).  The reference max a row's
 //    weights are taken against moves only when the tile max exceeds it by
 //    more than kRescaleSlack (so weights stay below 2^kRescaleSlack), and
 //    the accumulators are rescaled only in a step where some row's moved:
 //    after the first steps that is rare, and the result (acc / sum) does not
 //    depend on the reference.  P is rounded to bf16 for the product, and the
-//    running sum adds the same rounded values.
+//    running sum adds the same rounded values (v_dot2_f32_bf16 with (1, 1)).
 //  * O^T[128 dims x 16 rows] += V^T . P^T, eight v_mfma_f32_16x16x32_bf16
 //    (one per c = 0..7).  The 32 keys of the k-dimension are ordered so that
 //    lane l's eight P values are exactly its B operand: k = 8g+i is key 4g+i
@@ -52,6 +55,7 @@ constexpr int kPD = 128;                      // head_dim
 constexpr int kPRow = kPD * 2;                // bytes of one token row
 constexpr int kKeys = 32;                     // keys per step
 constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRowTiles = 2;                  // 16-row MFMA tiles per wave
 constexpr int kRowsPerWave = 16 * kRowTiles;
 static_assert(kWaves * kRowsPerWave == kPrefillRowsPerWg, "rows per workgroup");
@@ -61,6 +65,10 @@ constexpr int kKStride = kPRow + 16;
 constexpr int kKBytes = kKeys * kKStride;
 constexpr int kVBytes = kKeys * kPRow;
 constexpr int kBufBytes = kKBytes + kVBytes;
+// Steps whose K/V loads are in flight ahead of the step being computed; the
+// workgroup holds kDepth + 1 LDS buffers.
+constexpr int kDepth = 1;
+constexpr int kBufs = kDepth + 1;
 // Block-table entries held in LDS at a time (refilled every
 // kTableCap * BS / kKeys steps).
 constexpr int kTableCap = 1024;
@@ -83,14 +91,16 @@ __device__ __forceinline__ uint32_t pair16(const u32x4& a, const u32x4& b, int e
 }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// (1, 1) in bf16, for pair sums with v_dot2_f32_bf16.
+__device__ constexpr bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 // Two floats to two bf16 (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 template <int BS>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2][kBufBytes];
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kBufs][kBufBytes];
   __shared__ int32_t tab[kTableCap];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -121,7 +131,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int wrow0 = row0 + wave * kRowsPerWave;
   const bool wave_rows = wrow0 < rows;
   const int wave_pmax = wave_rows ? L - nq + (min(wrow0 + kRowsPerWave, rows) - 1) / G : -1;
+  const int wave_pmin = L - nq + wrow0 / G;      // lowest position of a row in this wave
 
+  // The weights are 2^(cexp s - m), cexp = |scale log2(e)| >= 0: a negative
+  // scale flips the sign of q instead (exact in bf16).
+  const float cexp = fabsf(a.scale_log2);
+  const u32x4 qsign = a.scale_log2 < 0.f ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}
+                                         : u32x4{0u, 0u, 0u, 0u};
   // This lane's row of each tile: position and Q^T operand (dims 32c+8g..+8).
   int pos[kRowTiles];
   u32x4 qop[kRowTiles][4];
@@ -136,7 +152,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     const char* row = qbase + ((int64_t)(q0 + token) * HQ + head) * kPRow + g4 * 16;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      qop[rt][c] = real ? *reinterpret_cast<const u32x4*>(row + c * 64) : u32x4{0u, 0u, 0u, 0u};
+      qop[rt][c] = real ? *reinterpret_cast<const u32x4*>(row + c * 64) ^ qsign
+                        : u32x4{0u, 0u, 0u, 0u};
   }
 
   // Block-table entries [first, first + kTableCap) of the blocks the keys up
@@ -145,40 +162,43 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int used_blocks = min(L, p_max + kKeys) / BS + 1;   // bound; only entries < ceil(L/BS) are read
   const int table_len = min(used_blocks, (L + BS - 1) / BS);
   auto stage_table = [&](int first) {
-    for (int i = tid; i < kTableCap && first + i < table_len; i += 256) tab[i] = table[first + i];
+    for (int i = tid; i < kTableCap && first + i < table_len; i += kThreads) tab[i] = table[first + i];
   };
   constexpr int kStepsPerTable = kTableCap * BS / kKeys;
   stage_table(0);
   __syncthreads();
 
-  // Step loads: thread tid moves key (tid/16) + 16h of the step, 16 bytes
-  // (dims 8*(tid%16)..+8), for h = 0, 1; keys at or past L load zeros.
+  // Step loads: thread tid moves key tid/16 + (kThreads/16) h of the step,
+  // 16 bytes (dims 8*(tid%16)..+8), for h < kLoads; keys at or past L load
+  // zeros.
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
+  constexpr int kKeysPerPass = kThreads / 16;
+  constexpr int kLoads = kKeys / kKeysPerPass;
   const int key_in_step = tid >> 4;
   const int chunk = (tid & 15) * 16;
-  u32x4 kr[2], vr[2];
-  auto fetch = [&](int k0) {
+  u32x4 kr[kDepth][kLoads], vr[kDepth][kLoads];
+  auto fetch = [&](int k0, int slot) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kk = k0 + key_in_step + 16 * h;
+    for (int h = 0; h < kLoads; ++h) {
+      const int kk = k0 + key_in_step + kKeysPerPass * h;
       if (kk < L) {
         const int64_t blk = tab[(kk / BS) % kTableCap];
         const int64_t off = (((blk * HKV + hk) * BS) + (kk % BS)) * kPRow + chunk;
-        kr[h] = *reinterpret_cast<const u32x4*>(kc + off);
-        vr[h] = *reinterpret_cast<const u32x4*>(vc + off);
+        kr[slot][h] = *reinterpret_cast<const u32x4*>(kc + off);
+        vr[slot][h] = *reinterpret_cast<const u32x4*>(vc + off);
       } else {
-        kr[h] = u32x4{0u, 0u, 0u, 0u};
-        vr[h] = u32x4{0u, 0u, 0u, 0u};
+        kr[slot][h] = u32x4{0u, 0u, 0u, 0u};
+        vr[slot][h] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int slot, int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = key_in_step + 16 * h;
-      lds_store16(lds[buf], key * kKStride + chunk, kr[h]);
-      lds_store16(lds[buf] + kKBytes, key * kPRow + chunk, vr[h]);
+    for (int h = 0; h < kLoads; ++h) {
+      const int key = key_in_step + kKeysPerPass * h;
+      lds_store16(lds[buf], key * kKStride + chunk, kr[slot][h]);
+      lds_store16(lds[buf] + kKBytes, key * kPRow + chunk, vr[slot][h]);
     }
   };
 
@@ -192,22 +212,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int c = 0; c < 8; ++c) acc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  fetch(0);
-  stash(0);
+  // Step j's rows travel in register slot j % kDepth and LDS buffer
+  // j % kBufs.  The slot is free again once step j is stashed, the buffer
+  // once step j is computed (kBufs - 1 iterations before it is refilled).
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j)
+    if (j < steps) fetch(j * kKeys, j);
+  stash(0, 0);
   __syncthreads();
   for (int t = 0; t < steps; ++t) {
     const int k0 = t * kKeys;
-    if (t + 1 < steps && (t + 1) % kStepsPerTable == 0) {
-      // The next step's keys need the next table window: every thread has
-      // finished reading the current one (its last fetch was the previous
-      // step's), so refill it between two barriers.
-      __syncthreads();
-      stage_table((t + 1) / kStepsPerTable * kTableCap);
-      __syncthreads();
+    const int ahead = t + kDepth;
+    if (ahead < steps) {
+      if (ahead % kStepsPerTable == 0) {
+        // Step `ahead` needs the next table window; every fetch of the
+        // current one has been issued, so refill it between two barriers.
+        __syncthreads();
+        stage_table(ahead / kStepsPerTable * kTableCap);
+        __syncthreads();
+      }
+      fetch(ahead * kKeys, t % kDepth);
     }
-    if (t + 1 < steps) fetch(k0 + kKeys);
     if (wave_rows && k0 <= wave_pmax) {
-      const char* kb = lds[t & 1];
+      // Some key of the step lies past some row's position (this includes
+      // every key at or past L).
+      const bool diagonal = k0 + kKeys - 1 > wave_pmin;
+      const char* kb = lds[t % kBufs];
       const char* vb = kb + kKBytes;
       // A operands of K . Q^T: key 16*half + n, dims 32c + 8g..+8.
       u32x4 kop[2][4];
@@ -229,31 +259,45 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       for (int c = 0; c < 8; ++c)
         va[c] = u32x4{pair16(vrow[0], vrow[1], c), pair16(vrow[2], vrow[3], c),
                       pair16(vrow[4], vrow[5], c), pair16(vrow[6], vrow[7], c)};
+      // Scores of both row tiles first, the four independent accumulators
+      // interleaved, so one tile's softmax overlaps the other's products.
+      f32x4_t scores[kRowTiles][2];
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) scores[rt][half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+            scores[rt][half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, kop[half][c]),
+                __builtin_bit_cast(bf16x8_t, qop[rt][c]), scores[rt][half], 0, 0, 0);
 #pragma unroll
       for (int rt = 0; rt < kRowTiles; ++rt) {
-        f32x4_t sc[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          sc[half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, kop[half][c]),
-                __builtin_bit_cast(bf16x8_t, qop[rt][c]), sc[half], 0, 0, 0);
-        }
-        // Scores in the exp2 domain, masked past the row's position.
+        const f32x4_t* sc = scores[rt];
+        // Raw scores.  On steps that reach past the wave's lowest row
+        // position (a wave-uniform branch), keys past a row's position are
+        // set to -inf: left out of the max, weight 0 below.
         float x[8];
-        float mx = -INFINITY;
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = k0 + 16 * half + 4 * g4 + i;
-            const float v = key <= pos[rt] ? sc[half][i] * a.scale_log2 : -INFINITY;
-            x[4 * half + i] = v;
-            mx = fmaxf(mx, v);
-          }
+          for (int i = 0; i < 4; ++i) x[4 * half + i] = sc[half][i];
+        if (diagonal) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (k0 + 16 * half + 4 * g4 + i > pos[rt]) x[4 * half + i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         mx = group4_max(mx);
+        // Tile max in the exp2 domain (cexp >= 0 keeps the order).
+        mx = mx == -INFINITY ? -INFINITY : mx * cexp;
         const bool grow = mx > m_run[rt] + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(grow)) {
           const float m_new = grow ? mx : m_run[rt];
@@ -261,16 +305,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
           m_run[rt] = m_new;
           l_run[rt] *= alpha;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) acc[rt][c] *= alpha;
+          for (int cc = 0; cc < 8; ++cc) acc[rt][cc] *= alpha;
         }
+        // Weights 2^(cexp x - m), rounded to bf16; the running sum adds the
+        // rounded pairs with one dot product each.
         uint32_t pb[4];
-        float psum = 0.f;
+        const float neg_m = -m_run[rt];
+        // x = -inf gives 2^-inf = 0 for cexp > 0; with cexp == 0 the product
+        // would be NaN, so masked weights are zeroed explicitly then.
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = fast_exp2(fmaf(x[j], cexp, neg_m));
+        if (diagonal && cexp == 0.f) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = x[j] == -INFINITY ? 0.f : w[j];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          pb[j] = cvt_bf16x2(fast_exp2(x[2 * j] - m_run[rt]), fast_exp2(x[2 * j + 1] - m_run[rt]));
-          psum += bf_lo(pb[j]) + bf_hi(pb[j]);
+          pb[j] = cvt_bf16x2(w[2 * j], w[2 * j + 1]);
+          l_run[rt] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pb[j]), kOnes, l_run[rt], false);
         }
-        l_run[rt] += psum;
         const u32x4 pop = u32x4{pb[0], pb[1], pb[2], pb[3]};
 #pragma unroll
         for (int c = 0; c < 8; ++c)
@@ -279,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
               0, 0, 0);
       }
     }
-    if (t + 1 < steps) stash((t + 1) & 1);
+    if (t + 1 < steps) stash((t + 1) % kDepth, (t + 1) % kBufs);
     __syncthreads();
   }
 
@@ -314,9 +368,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int block_size, hipStream_t stre
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (block_size == 16)
-    hipLaunchKernelGGL(prefill_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(prefill_kernel<16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(prefill_kernel<32>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

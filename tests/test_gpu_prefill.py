@@ -77,6 +77,16 @@ def test_long_context_crosses_table_windows(bs):
     say("max-abs %.3e row-rel %.3e" % err)
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+def test_any_scale(scale):
+    """A negative scale (the kernel flips q's sign), zero (uniform weights
+    over the visible keys) and a large one (peaked weights)."""
+    w = wl.make_prefill("scale", 630, wl.BF16, 8, 2, 128, 16, [70, 33, 200], [70, 5, 64])
+    w = wl.PrefillWorkload(**{**w.__dict__, "scale": np.float32(scale)})
+    got = out_f64(run_device(w))
+    assert_attention_close(got, oracle_rows(w), wl.BF16)
+
+
 def test_max_query_len_larger_than_needed_changes_nothing():
     w = wl.make_prefill("slack", 611, wl.BF16, 8, 2, 128, 16, [90, 40, 7], [90, 12, 7])
     a = run_device(w)
