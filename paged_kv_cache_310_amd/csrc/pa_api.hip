@@ -372,7 +372,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   const int group = num_q_heads / num_kv_heads;
   const int64_t tiles =
       ((int64_t)max_query_len * group + pa::kPrefillRowsPerWg - 1) / pa::kPrefillRowsPerWg;
-  if (tiles * num_seqs * num_kv_heads > INT32_MAX || num_query_tokens * num_q_heads > INT32_MAX)
+  const int64_t pair_rounds = ((int64_t)num_seqs * num_kv_heads + pa::kNumXcd - 1) / pa::kNumXcd;
+  if (tiles * pa::kNumXcd * pair_rounds > INT32_MAX || num_query_tokens * num_q_heads > INT32_MAX)
     return PA_ERR_UNSUPPORTED;
 
   hipStream_t st = static_cast<hipStream_t>(stream);

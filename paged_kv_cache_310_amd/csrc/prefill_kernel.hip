@@ -9,9 +9,11 @@
 // i of an n-token chunk sits at position L - n + i of the L cached tokens and
 // attends to positions 0..L - n + i, gathered through the sequence's table.
 //
-// Work: one workgroup (kWaves waves) per kWaves * 32 query rows of one (sequence, KV
-// head).  A row is a (query token, query head) pair of the KV head's group,
-// token-major, so grouped query heads share every K/V tile.  Each wave owns
+// Work: one workgroup (kWaves waves) per kWaves * 32 query rows of one
+// (sequence, KV head) pair, the pairs dealt to the XCDs so that a pair's
+// workgroups share its K/V in one L2.  A row is a (query token, query
+// head) pair of the KV head's group, token-major, so grouped query heads
+// share every K/V tile.  Each wave owns
 // 32 rows as two 16-row MFMA tiles.  The workgroup walks the keys in steps of
 // 32 (two 16-token halves): all threads load a step's K and V rows through
 // the table into registers kDepth steps ahead and store them to one of
@@ -111,11 +113,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
   const int HQ = a.num_q_heads;
   const int G = a.group;
 
-  // The last row tiles of every (sequence, KV head) see the most keys under
-  // the causal mask: they are dispatched first.
+  // Workgroup ids are dealt round-robin to the 8 XCDs (each with its own
+  // L2).  XCD x (ids congruent to x mod 8) takes the (sequence, KV head)
+  // pairs x, x + 8, ..., and each pair's row tiles back to back, heaviest
+  // (last, seeing the most keys under the causal mask) first: the tiles of a
+  // pair run on one XCD at about the same time and share its K/V through
+  // that XCD's L2 instead of each fetching it from HBM.  Dealing pairs
+  // round-robin keeps the XCDs' shares of every sequence equal.
   const int pairs = a.num_seqs * HKV;
-  const int tile = a.tiles_per_seq - 1 - (int)blockIdx.x / pairs;
-  const int pair = (int)blockIdx.x % pairs;
+  const int xcd = (int)blockIdx.x % kNumXcd;
+  const int slot = (int)blockIdx.x / kNumXcd;
+  const int pair = (slot / a.tiles_per_seq) * kNumXcd + xcd;
+  const int tile = a.tiles_per_seq - 1 - slot % a.tiles_per_seq;
+  if (pair >= pairs) return;
   const int s = pair / HKV;
   const int hk = pair % HKV;
   const int q0 = a.query_start[s];
@@ -159,10 +169,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
   // Block-table entries [first, first + kTableCap) of the blocks the keys up
   // to p_max use, staged in LDS.
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int used_blocks = min(L, p_max + kKeys) / BS + 1;   // bound; only entries < ceil(L/BS) are read
+  // Keys fetched stay below min(L, p_max + kKeys); entries past
+  // ceil(L / BS) are never read.
+  const int used_blocks = min(L, p_max + kKeys) / BS + 1;
   const int table_len = min(used_blocks, (L + BS - 1) / BS);
   auto stage_table = [&](int first) {
-    for (int i = tid; i < kTableCap && first + i < table_len; i += kThreads) tab[i] = table[first + i];
+    for (int i = tid; i < kTableCap && first + i < table_len; i += kThreads)
+      tab[i] = table[first + i];
   };
   constexpr int kStepsPerTable = kTableCap * BS / kKeys;
   stage_table(0);
@@ -364,7 +377,9 @@ bool prefill_supported(int dtype, int head_dim, int block_size) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int block_size, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.tiles_per_seq * a.num_seqs * a.num_kv_heads;
+  // Whole rounds of 8 pairs: workgroups past the last pair leave at once.
+  const int64_t blocks =
+      (int64_t)a.tiles_per_seq * kNumXcd * ((a.num_seqs * a.num_kv_heads + kNumXcd - 1) / kNumXcd);
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (block_size == 16)
