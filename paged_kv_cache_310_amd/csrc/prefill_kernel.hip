@@ -11,17 +11,17 @@
 //
 // Work: one workgroup (kWaves waves) per kWaves * 32 query rows of one
 // (sequence, KV head) pair, the pairs dealt to the XCDs so that a pair's
-// workgroups share its K/V in one L2.  A row is a (query token, query
-// head) pair of the KV head's group, token-major, so grouped query heads
-// share every K/V tile.  Each wave owns
-// 32 rows as two 16-row MFMA tiles.  The workgroup walks the keys in steps of
-// 32 (two 16-token halves): all threads load a step's K and V rows through
-// the table into registers kDepth steps ahead and store them to one of
-// kDepth + 1 LDS buffers after the step before it is computed, so the global
-// loads of the next steps overlap the products of this one and one barrier
-// per step suffices.  The sequence's block-table
-// entries are staged in LDS (kTableCap at a time), so no step waits on a
-// table read before it can address its K/V rows.
+// workgroups share its K/V in one L2.  A row is a (query token, query head)
+// pair of the KV head's group, token-major, so grouped query heads share
+// every K/V tile.  Each wave owns 32 rows as two 16-row MFMA tiles,
+// interleaved with the other waves' tiles.  The workgroup walks the keys in
+// steps of 32 (two 16-token halves): all threads load a step's K and V rows
+// through the table into registers kDepth steps ahead and store them to one
+// of kDepth + 1 LDS buffers after the step before it is computed, so the
+// global loads of the next steps overlap the products of this one and one
+// barrier per step suffices.  The sequence's block-table entries are staged
+// in LDS (kTableCap at a time), so no step waits on a table read before it
+// can address its K/V rows.
 //
 // Per step and 16-row tile (lane l, lane group g = l/16, column n = l%16):
 //  * S^T[16 keys x 16 rows] = K . Q^T for each 16-key half, four
@@ -138,10 +138,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
   const int p_max = L - nq + last_row / G;       // highest position a row here has
   const int steps = p_max / kKeys + 1;
 
-  const int wrow0 = row0 + wave * kRowsPerWave;
-  const bool wave_rows = wrow0 < rows;
-  const int wave_pmax = wave_rows ? L - nq + (min(wrow0 + kRowsPerWave, rows) - 1) / G : -1;
-  const int wave_pmin = L - nq + wrow0 / G;      // lowest position of a row in this wave
+  // Row tile rt of wave w covers rows row0 + 16 (rt kWaves + w) .. +16: the
+  // waves' tiles interleave, so under the causal mask the waves of a
+  // workgroup see nearly the same number of keys.
+  auto tile_row0 = [&](int rt) { return row0 + 16 * (rt * kWaves + wave); };
+  const bool wave_rows = tile_row0(0) < rows;
+  int wave_last = -1;                              // last real row of this wave
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt)
+    if (tile_row0(rt) < rows) wave_last = min(tile_row0(rt) + 15, rows - 1);
+  const int wave_pmax = wave_rows ? L - nq + wave_last / G : -1;
+  const int wave_pmin = L - nq + tile_row0(0) / G;   // lowest position of a row in this wave
 
   // The weights are 2^(cexp s - m), cexp = |scale log2(e)| >= 0: a negative
   // scale flips the sign of q instead (exact in bf16).
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
   const char* qbase = static_cast<const char*>(a.q);
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
-    const int r = wrow0 + 16 * rt + n;
+    const int r = tile_row0(rt) + n;
     const bool real = r < rows;
     const int token = real ? r / G : 0;
     const int head = hk * G + (real ? r % G : 0);
@@ -355,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
     const float total = group4_sum(l_run[rt]);
-    const int r = wrow0 + 16 * rt + n;
+    const int r = tile_row0(rt) + n;
     if (r >= rows) continue;
     const float inv = 1.f / total;
     char* row = obase + ((int64_t)(q0 + r / G) * HQ + hk * G + r % G) * kPRow + g4 * 64;
