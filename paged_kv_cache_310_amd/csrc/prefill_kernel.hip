@@ -42,10 +42,10 @@
 //  * O^T[128 dims x 16 rows] += V^T . P^T, eight v_mfma_f32_16x16x32_bf16
 //    (one per c = 0..7).  The 32 keys of the k-dimension are ordered so that
 //    lane l's eight P values are exactly its B operand: k = 8g+i is key 4g+i
-//    and k = 8g+4+i is key 16+4g+i.  The A operand of MFMA c is element c of
-//    eight 16-byte LDS reads of V (lane l: those eight keys, dims 8n..8n+7),
-//    so MFMA c produces dims 8m + c and lane l ends up holding the 32
-//    contiguous dims 32g..32g+31 of row n.
+//    and k = 8g+4+i is key 16+4g+i.  The A operand of MFMA c (dims
+//    16c..16c+15) comes from two transposing LDS reads (ds_read_b64_tr_b16)
+//    of the row-major V tile, so lane l ends up holding dims 16c + 4g + i of
+//    row n.
 #include "decode_common.h"
 
 namespace pa {
@@ -65,7 +65,10 @@ static_assert(kWaves * kRowsPerWave == kPrefillRowsPerWg, "rows per workgroup");
 // touches then start on 16 different 4-bank groups.
 constexpr int kKStride = kPRow + 16;
 constexpr int kKBytes = kKeys * kKStride;
-constexpr int kVBytes = kKeys * kPRow;
+// V rows are padded by 32 bytes: the 16 rows one transposing read touches
+// (32 bytes each) then fill the 64 banks exactly twice.
+constexpr int kVStride = kPRow + 32;
+constexpr int kVBytes = kKeys * kVStride;
 constexpr int kBufBytes = kKBytes + kVBytes;
 // Steps whose K/V loads are in flight ahead of the step being computed; the
 // workgroup holds kDepth + 1 LDS buffers.
@@ -86,10 +89,15 @@ __device__ __forceinline__ void lds_store16(char* base, int offset, const u32x4&
   *reinterpret_cast<u32x4*>(base + offset) = v;
 }
 
-// Element e (bf16) of fragment a in the low half, of fragment b in the high
-// half: one v_perm_b32.
-__device__ __forceinline__ uint32_t pair16(const u32x4& a, const u32x4& b, int e) {
-  return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+typedef short i16x4_t_lds __attribute__((ext_vector_type(4)));
+typedef i16x4_t_lds __attribute__((address_space(3))) lds_i16x4;
+// ds_read_b64_tr_b16: within each 16-lane group, lane j receives element j % 4
+// of the 8-byte fragments that lanes 4e + j / 4 (e = 0..3) address, as its
+// element e.
+__device__ __forceinline__ uint64_t lds_read_tr16(const char* base, int offset) {
+  const i16x4_t_lds v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(const_cast<char*>(base) + offset));
+  return __builtin_bit_cast(uint64_t, v);
 }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -218,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
     for (int h = 0; h < kLoads; ++h) {
       const int key = key_in_step + kKeysPerPass * h;
       lds_store16(lds[buf], key * kKStride + chunk, kr[slot][h]);
-      lds_store16(lds[buf] + kKBytes, key * kPRow + chunk, vr[slot][h]);
+      lds_store16(lds[buf] + kKBytes, key * kVStride + chunk, vr[slot][h]);
     }
   };
 
@@ -266,19 +274,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           kop[half][c] = lds_load16(kb, (16 * half + n) * kKStride + c * 64 + g4 * 16);
-      // V rows of this lane's eight keys (k = 8g..8g+7), dims 8n..8n+7.
-      u32x4 vrow[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = (j < 4) ? 4 * g4 + j : 16 + 4 * g4 + (j - 4);
-        vrow[j] = lds_load16(vb, key * kPRow + n * 16);
-      }
-      // A operands of V^T . P^T: element c of the eight rows (dim 8n + c).
+      // A operands of V^T . P^T for dim tile c (dims 16c..16c+15): lane n
+      // of group g needs V[key][16c + n] for its eight keys (k = 8g..8g+7:
+      // keys 4g..4g+3, then 16+4g..16+4g+3).  In each of two transposing
+      // reads, lane n of the group addresses key 4g + n/4 (+16), dims
+      // 16c + 4(n%4)..+4, and receives V[4g + e (+16)][16c + n], e = 0..3.
       u32x4 va[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        va[c] = u32x4{pair16(vrow[0], vrow[1], c), pair16(vrow[2], vrow[3], c),
-                      pair16(vrow[4], vrow[5], c), pair16(vrow[6], vrow[7], c)};
+      for (int c = 0; c < 8; ++c) {
+        const int col = (16 * c + 4 * (n & 3)) * 2;
+        const uint64_t lo = lds_read_tr16(vb, (4 * g4 + (n >> 2)) * kVStride + col);
+        const uint64_t hi = lds_read_tr16(vb, (16 + 4 * g4 + (n >> 2)) * kVStride + col);
+        va[c] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+      }
       // Scores of both row tiles first, the four independent accumulators
       // interleaved, so one tile's softmax overlaps the other's products.
       f32x4_t scores[kRowTiles][2];
@@ -357,7 +365,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
     __syncthreads();
   }
 
-  // Normalise and store: lane l holds dims 32g + 8i + c (c = 0..7) of its row.
+  // Normalise and store: lane l holds dims 16c + 4g + i (i = 0..3) of its
+  // row in acc[rt][c].
   char* obase = static_cast<char*>(a.out);
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
@@ -365,14 +374,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
     const int r = tile_row0(rt) + n;
     if (r >= rows) continue;
     const float inv = 1.f / total;
-    char* row = obase + ((int64_t)(q0 + r / G) * HQ + hk * G + r % G) * kPRow + g4 * 64;
+    char* row = obase + ((int64_t)(q0 + r / G) * HQ + hk * G + r % G) * kPRow + g4 * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        v[j] = cvt_bf16x2(acc[rt][2 * j][i] * inv, acc[rt][2 * j + 1][i] * inv);
-      *reinterpret_cast<u32x4*>(row + i * 16) = v;
+    for (int c = 0; c < 8; ++c) {
+      const uint2 v = make_uint2(cvt_bf16x2(acc[rt][c][0] * inv, acc[rt][c][1] * inv),
+                                 cvt_bf16x2(acc[rt][c][2] * inv, acc[rt][c][3] * inv));
+      *reinterpret_cast<uint2*>(row + c * 32) = v;
     }
   }
 }
