@@ -40,7 +40,8 @@
 //    depend on the reference.  P is rounded to bf16 for the product, and the
 //    running sum adds the same rounded values (v_dot2_f32_bf16 with (1, 1)).
 //  * O^T[128 dims x 16 rows] += V^T . P^T, eight v_mfma_f32_16x16x32_bf16
-//    (one per c = 0..7).  The 32 keys of the k-dimension are ordered so that
+//    (one per c = 0..7) per row tile, issued after both tiles' softmax so
+//    that one V^T operand read serves both tiles.  The 32 keys of the k-dimension are ordered so that
 //    lane l's eight P values are exactly its B operand: k = 8g+i is key 4g+i
 //    and k = 8g+4+i is key 16+4g+i.  The A operand of MFMA c (dims
 //    16c..16c+15) comes from two transposing LDS reads (ds_read_b64_tr_b16)
@@ -109,7 +110,9 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 }
 
 template <int BS>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs a) {
+// Three workgroups (12 waves) per CU: the register budget this sets (168)
+// costs a few spilled registers and measured faster than two workgroups.
+__global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kBufs][kBufBytes];
   __shared__ int32_t tab[kTableCap];
   const int tid = threadIdx.x;
@@ -267,26 +270,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
       const bool diagonal = k0 + kKeys - 1 > wave_pmin;
       const char* kb = lds[t % kBufs];
       const char* vb = kb + kKBytes;
-      // A operands of K . Q^T: key 16*half + n, dims 32c + 8g..+8.
-      u32x4 kop[2][4];
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          kop[half][c] = lds_load16(kb, (16 * half + n) * kKStride + c * 64 + g4 * 16);
-      // A operands of V^T . P^T for dim tile c (dims 16c..16c+15): lane n
-      // of group g needs V[key][16c + n] for its eight keys (k = 8g..8g+7:
-      // keys 4g..4g+3, then 16+4g..16+4g+3).  In each of two transposing
-      // reads, lane n of the group addresses key 4g + n/4 (+16), dims
-      // 16c + 4(n%4)..+4, and receives V[4g + e (+16)][16c + n], e = 0..3.
-      u32x4 va[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      // V^T operand of dim tile c (dims 16c..16c+15): lane n of group g
+      // needs V[key][16c + n] for its eight keys (k = 8g..8g+7: keys
+      // 4g..4g+3, then 16+4g..16+4g+3).  In each of two transposing reads,
+      // lane n of the group addresses key 4g + n/4 (+16), dims 16c + 4(n%4)
+      // ..+4, and receives V[4g + e (+16)][16c + n], e = 0..3.
+      auto v_operand = [&](int c) {
         const int col = (16 * c + 4 * (n & 3)) * 2;
         const uint64_t lo = lds_read_tr16(vb, (4 * g4 + (n >> 2)) * kVStride + col);
         const uint64_t hi = lds_read_tr16(vb, (16 + 4 * g4 + (n >> 2)) * kVStride + col);
-        va[c] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
-      }
+        return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+      };
       // Scores of both row tiles first, the four independent accumulators
       // interleaved, so one tile's softmax overlaps the other's products.
       f32x4_t scores[kRowTiles][2];
@@ -295,14 +289,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
 #pragma unroll
         for (int half = 0; half < 2; ++half) scores[rt][half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c) {
+        // K operands of dims 32c + 8g..+8: key 16*half + n.
+        u32x4 kop[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          kop[half] = lds_load16(kb, (16 * half + n) * kKStride + c * 64 + g4 * 16);
 #pragma unroll
         for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
           for (int half = 0; half < 2; ++half)
             scores[rt][half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, kop[half][c]),
+                __builtin_bit_cast(bf16x8_t, kop[half]),
                 __builtin_bit_cast(bf16x8_t, qop[rt][c]), scores[rt][half], 0, 0, 0);
+      }
+      u32x4 pop[kRowTiles];
 #pragma unroll
       for (int rt = 0; rt < kRowTiles; ++rt) {
         const f32x4_t* sc = scores[rt];
@@ -353,12 +354,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
           pb[j] = cvt_bf16x2(w[2 * j], w[2 * j + 1]);
           l_run[rt] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pb[j]), kOnes, l_run[rt], false);
         }
-        const u32x4 pop = u32x4{pb[0], pb[1], pb[2], pb[3]};
+        pop[rt] = u32x4{pb[0], pb[1], pb[2], pb[3]};
+      }
+      // O^T += V^T . P^T, one V^T operand per dim tile for both row tiles.
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < 8; ++c) {
+        const u32x4 va = v_operand(c);
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt)
           acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, va[c]), __builtin_bit_cast(bf16x8_t, pop), acc[rt][c],
-              0, 0, 0);
+              __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pop[rt]),
+              acc[rt][c], 0, 0, 0);
       }
     }
     if (t + 1 < steps) stash((t + 1) % kDepth, (t + 1) % kBufs);
