@@ -104,6 +104,17 @@ int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
  * allocation takes it). */
 int pa_bm_free_sequence(pa_bm* bm, int64_t seq);
 
+/* Batched pa_bm_fork: registers children[i] sharing every block of
+ * parents[i], for i in [0, n) in order, so a child made by an earlier pair may
+ * be the parent of a later one.  Checked before anything changes: every
+ * parent known (or made earlier in the batch), every child new and listed
+ * once; a failure changes nothing. */
+int pa_bm_fork_many(pa_bm* bm, const int64_t* parents, const int64_t* children, int64_t n);
+
+/* Batched pa_bm_free_sequence over n distinct registered sequences (a
+ * sequence listed twice is PA_BM_INVALID); a failure changes nothing. */
+int pa_bm_free_many(pa_bm* bm, const int64_t* seqs, int64_t n);
+
 /* Length of a registered sequence. */
 int pa_bm_length(const pa_bm* bm, int64_t seq, int64_t* length);
 

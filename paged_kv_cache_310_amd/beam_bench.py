@@ -4,8 +4,9 @@
 Workload (LLaMA-13B-shaped heads: 40 KV heads, head_dim 128, bf16, 16-token
 blocks): 16 requests, each a 1000-token prompt (so its last prompt block is
 partly filled) searched with 8 beams.  Every step keeps 2 seeded survivors per
-request, forks each back to 8 beams, asks the host block manager (libpabm.so)
-for the slots and copy-on-write pairs, and runs pa_copy_blocks and a fused
+request, forks each back to 8 beams (one batched free and one batched fork
+call for all requests), asks the host block manager (libpabm.so) for the
+slots and copy-on-write pairs, and runs pa_copy_blocks and a fused
 append + pa_decode for all 128 beams.
 
 Reported per step: wall-clock time of the whole step (host manager + uploads
@@ -77,22 +78,23 @@ def main():
     def step(sample: bool, timed: bool):
         nonlocal next_id
         t0 = time.perf_counter()
-        live = []
+        live, dead, parents, children = [], [], [], []
         for r in range(a.requests):
             group = beams[r]
             survivors = sorted(rng.choice(group, size=a.keep, replace=False).tolist())
-            for s in group:
-                if s not in survivors:
-                    mgr.free_sequence(s)
+            dead.extend(s for s in group if s not in survivors)
             group = []
             for s in survivors:
                 group.append(s)
                 for _ in range(a.width // a.keep - 1):
-                    mgr.fork(s, next_id)
+                    parents.append(s)
+                    children.append(next_id)
                     group.append(next_id)
                     next_id += 1
             beams[r] = group
             live.extend(group)
+        mgr.free_many(dead)
+        mgr.fork_many(parents, children)
         slots, copies = mgr.append_slots(live)
         tables, lens = mgr.block_tables(live, max_blocks=max_blocks)
         t1 = time.perf_counter()

@@ -6,8 +6,8 @@ step makes; prints one JSON line.  ``python -m paged_kv_cache_310_amd.bm_bench``
 * prefix admission: 64 sequences that share a 1024-token prompt prefix, each
   registered with its token ids (the first allocates, the rest reuse);
 * beam churn: 32 beams per request, each step forks the 8 best beams 4 ways,
-  frees the rest and appends one token to every beam (copy-on-write of the
-  shared tail blocks).
+  frees the rest (one batched free and one batched fork call) and appends one
+  token to every beam (copy-on-write of the shared tail blocks).
 Times are host wall clock, median of repeats, in microseconds.
 """
 
@@ -83,15 +83,16 @@ def beam_churn(beams: int = 32, keep: int = 8, steps: int = 64, prompt: int = 50
         t0 = time.perf_counter()
         for _ in range(steps):
             survivors, dead = live[:keep], live[keep:]
-            for s in dead:
-                m.free_sequence(s)
-            live = []
+            m.free_many(dead)
+            live, parents, children = [], [], []
             for s in survivors:
                 live.append(s)
                 for _ in range(beams // keep - 1):
-                    m.fork(s, nxt)
+                    parents.append(s)
+                    children.append(nxt)
                     live.append(nxt)
                     nxt += 1
+            m.fork_many(parents, children)
             m.append_slots(live)
         run.elapsed = time.perf_counter() - t0
 

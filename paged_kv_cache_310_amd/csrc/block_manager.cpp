@@ -392,6 +392,62 @@ int pa_bm_free_sequence(pa_bm* bm, int64_t seq) {
   return PA_BM_OK;
 }
 
+int pa_bm_fork_many(pa_bm* bm, const int64_t* parents, const int64_t* children, int64_t n) {
+  if (bm == nullptr || n < 0 || (n > 0 && (parents == nullptr || children == nullptr)))
+    return PA_BM_INVALID;
+  try {
+    // Check the whole batch first: pair i may fork a child made by an
+    // earlier pair, never an unknown sequence; every child is new.
+    std::unordered_map<int64_t, int64_t> made;   // child -> its parent in this batch
+    made.reserve((size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+      if (children[i] < 0) return PA_BM_INVALID;
+      if (!bm->seqs.count(parents[i]) && !made.count(parents[i])) return PA_BM_UNKNOWN_SEQ;
+      if (bm->seqs.count(children[i]) || made.count(children[i])) return PA_BM_EXISTS;
+      made.emplace(children[i], parents[i]);
+    }
+    int64_t done = 0;
+    try {
+      for (; done < n; ++done) {
+        Sequence c = bm->seqs.at(parents[done]);
+        for (int64_t b : c.table) ++bm->refcount[b];
+        bm->seqs.emplace(children[done], std::move(c));
+      }
+    } catch (const std::bad_alloc&) {
+      // Undo the pairs already applied, newest first.
+      for (int64_t i = done - 1; i >= 0; --i) {
+        auto it = bm->seqs.find(children[i]);
+        for (int64_t b : it->second.table) --bm->refcount[b];
+        bm->seqs.erase(it);
+      }
+      return PA_BM_NOMEM;
+    }
+    return PA_BM_OK;
+  } catch (const std::bad_alloc&) {
+    return PA_BM_NOMEM;
+  }
+}
+
+int pa_bm_free_many(pa_bm* bm, const int64_t* seqs, int64_t n) {
+  if (bm == nullptr || n < 0 || (n > 0 && seqs == nullptr)) return PA_BM_INVALID;
+  try {
+    std::unordered_map<int64_t, char> seen;
+    seen.reserve((size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+      if (!bm->seqs.count(seqs[i])) return PA_BM_UNKNOWN_SEQ;
+      if (!seen.emplace(seqs[i], 1).second) return PA_BM_INVALID;   // listed twice
+    }
+  } catch (const std::bad_alloc&) {
+    return PA_BM_NOMEM;
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    for (int64_t b : it->second.table) bm->release(b);
+    bm->seqs.erase(it);
+  }
+  return PA_BM_OK;
+}
+
 int pa_bm_length(const pa_bm* bm, int64_t seq, int64_t* length) {
   if (bm == nullptr || length == nullptr) return PA_BM_INVALID;
   auto it = bm->seqs.find(seq);

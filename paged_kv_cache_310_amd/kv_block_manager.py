@@ -66,6 +66,8 @@ def _load():
         lib.pa_bm_append_slots.argtypes = [vp, p64, p32, i64, p64, p64, p64]
         lib.pa_bm_fork.argtypes = [vp, i64, i64]
         lib.pa_bm_free_sequence.argtypes = [vp, i64]
+        lib.pa_bm_fork_many.argtypes = [vp, p64, p64, i64]
+        lib.pa_bm_free_many.argtypes = [vp, p64, i64]
         lib.pa_bm_length.argtypes = [vp, i64, p64]
         lib.pa_bm_block_tables.argtypes = [vp, p64, i64, i64, ctypes.c_int32, p32, p32]
         lib.pa_bm_refcount.argtypes = [vp, i64, p64]
@@ -76,7 +78,7 @@ def _load():
         lib.pa_bm_status_string.argtypes = [i32]
         lib.pa_bm_status_string.restype = ctypes.c_char_p
         for f in ("pa_bm_create", "pa_bm_add_sequence", "pa_bm_append_slots", "pa_bm_fork",
-                  "pa_bm_free_sequence", "pa_bm_length", "pa_bm_block_tables", "pa_bm_refcount",
+                  "pa_bm_free_sequence", "pa_bm_fork_many", "pa_bm_free_many", "pa_bm_length", "pa_bm_block_tables", "pa_bm_refcount",
                   "pa_bm_get_stats", "pa_bm_check"):
             getattr(lib, f).restype = i32
         _lib = lib
@@ -176,6 +178,20 @@ class KVBlockManager:
 
     def free_sequence(self, seq: int) -> None:
         _call("pa_bm_free_sequence", _load().pa_bm_free_sequence(self._h, int(seq)))
+
+    def fork_many(self, parents: Sequence[int], children: Sequence[int]) -> None:
+        """``fork(parents[i], children[i])`` for every i, in order, in one call
+        (all or nothing)."""
+        p, c = _i64(parents), _i64(children)
+        if p.size != c.size:
+            raise ValueError("one child per parent")
+        _call("pa_bm_fork_many", _load().pa_bm_fork_many(self._h, _p64(p), _p64(c), p.size))
+
+    def free_many(self, seqs: Sequence[int]) -> None:
+        """``free_sequence`` of every listed (distinct) sequence in one call
+        (all or nothing)."""
+        s = _i64(seqs)
+        _call("pa_bm_free_many", _load().pa_bm_free_many(self._h, _p64(s), s.size))
 
     def length(self, seq: int) -> int:
         out = ctypes.c_int64(0)

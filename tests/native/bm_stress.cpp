@@ -54,19 +54,47 @@ static int run(unsigned seed, int prefix_cache) {
       if (st != PA_BM_OK && st != PA_BM_EXHAUSTED) return fail("append", st);
       for (int64_t i = 0; st == PA_BM_OK && i < (int64_t)batch.size(); ++i)
         if (slots[i] < 0 || slots[i] >= nb * bs) return fail("slot range", PA_BM_CORRUPT);
-    } else if (kind == 2) {
+    } else if (kind == 2 && rng() % 2) {
       const int64_t p = live[rng() % live.size()];
       st = pa_bm_fork(bm, p, next_id);
       if (st) return fail("fork", st);
       live.push_back(next_id);
       toks.resize(next_id + 1);
       ++next_id;
-    } else {
+    } else if (kind == 2) {
+      // batched: up to three children, a later one may fork an earlier one
+      const int k = 1 + (int)(rng() % 3);
+      std::vector<int64_t> parents, children;
+      for (int j = 0; j < k; ++j) {
+        parents.push_back(j > 0 && rng() % 2 ? children.back() : live[rng() % live.size()]);
+        children.push_back(next_id + j);
+      }
+      st = pa_bm_fork_many(bm, parents.data(), children.data(), k);
+      if (st) return fail("fork_many", st);
+      for (int64_t c : children) live.push_back(c);
+      next_id += k;
+      toks.resize(next_id);
+    } else if (rng() % 2 || live.size() < 2) {
       const size_t i = rng() % live.size();
       st = pa_bm_free_sequence(bm, live[i]);
       if (st) return fail("free", st);
       live[i] = live.back();
       live.pop_back();
+    } else {
+      // batched: two distinct sequences, plus a rejected call listing one twice
+      const size_t i = rng() % live.size();
+      size_t j = rng() % (live.size() - 1);
+      if (j >= i) ++j;
+      const int64_t dup[2] = {live[i], live[i]};
+      if (pa_bm_free_many(bm, dup, 2) != PA_BM_INVALID) return fail("free_many dup", PA_BM_CORRUPT);
+      const int64_t two[2] = {live[i], live[j]};
+      st = pa_bm_free_many(bm, two, 2);
+      if (st) return fail("free_many", st);
+      const int64_t a = live[i], b = live[j];
+      std::vector<int64_t> rest;
+      for (int64_t x : live)
+        if (x != a && x != b) rest.push_back(x);
+      live.swap(rest);
     }
     st = pa_bm_check(bm);
     if (st) return fail("check", st);

@@ -237,6 +237,66 @@ def test_failing_calls_change_nothing():
     m.check()
 
 
+def _state(m, seqs, max_blocks):
+    tab, lens = m.block_tables(seqs, max_blocks)
+    refs = [m.refcount(b) for b in range(m.stats()["num_blocks"])]
+    return tab.tolist(), lens.tolist(), refs
+
+
+def test_batched_fork_and_free_equal_single_calls():
+    rng = np.random.default_rng(3)
+    order = np.random.default_rng(4).permutation(200)
+    a = kvb.KVBlockManager(200, 4, free_order=order)
+    b = kvb.KVBlockManager(200, 4, free_order=order)
+    for m in (a, b):
+        m.add_sequence(0, 13)
+        m.add_sequence(1, 6)
+    live, nxt = [0, 1], 2
+    for step in range(12):
+        parents = [int(p) for p in rng.choice(live, size=3)]
+        children = list(range(nxt, nxt + 3))
+        parents[2] = children[0]                 # a child made earlier in the batch
+        nxt += 3
+        for p, c in zip(parents, children):
+            a.fork(p, c)
+        b.fork_many(parents, children)
+        live += children
+        dead = [int(x) for x in rng.choice(live, size=2, replace=False)]
+        for d in dead:
+            a.free_sequence(d)
+        b.free_many(dead)
+        live = [x for x in live if x not in dead]
+        sa, ca = a.append_slots(live)
+        sb, cb = b.append_slots(live)
+        assert np.array_equal(sa, sb) and np.array_equal(ca, cb)
+        assert _state(a, live, 16) == _state(b, live, 16)
+        a.check()
+        b.check()
+
+
+def test_batched_calls_are_all_or_nothing():
+    m = kvb.KVBlockManager(16, 4)
+    m.add_sequence(0, 9)
+    m.add_sequence(1, 3)
+    before = (m.stats(), _state(m, [0, 1], 4))
+    cases = [
+        (lambda: m.fork_many([0, 7, 1], [2, 3, 4]), kvb.UNKNOWN_SEQ),   # unknown parent
+        (lambda: m.fork_many([0, 1], [2, 2]), kvb.EXISTS),              # child listed twice
+        (lambda: m.fork_many([0, 0], [2, 1]), kvb.EXISTS),              # child already registered
+        (lambda: m.fork_many([0, 3], [2, 4]), kvb.UNKNOWN_SEQ),         # parent made only later
+        (lambda: m.free_many([0, 5]), kvb.UNKNOWN_SEQ),
+        (lambda: m.free_many([1, 1]), kvb.INVALID),
+    ]
+    for call, status in cases:
+        with pytest.raises(kvb.BlockManagerError) as e:
+            call()
+        assert e.value.status == status
+        assert (m.stats(), _state(m, [0, 1], 4)) == before
+    m.fork_many([], [])
+    m.free_many([])
+    m.check()
+
+
 def test_fragmentation_numbers_of_the_pages():
     bs = GOLDEN["default_block_size"]["value"]
     lengths = list(range(1, 10 * bs))
