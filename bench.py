@@ -66,6 +66,9 @@ def parse():
                    help="extra steps, each after a 512 MiB write that evicts the MALL")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU oracle time budget for the baseline sample (0 = skip)")
+    p.add_argument("--prefill-workload", default=None,
+                   help="measure multi-token (prefill) attention on this workload instead "
+                        "(llama13b_prefill or gqa_chunked_prefill)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -135,6 +138,69 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def prefill_cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle's multi-token attention on query tokens of the
+    workload (all heads of each), in a fixed seeded order, in batches of 16
+    tokens until the time budget is used; rate in flop/s of the same
+    algorithmic count the GPU figure uses."""
+    import oracle
+    k, v = oracle.append_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, w.block_size)
+    starts = w.query_start.astype(np.int64)
+    seq_of = np.searchsorted(starts, np.arange(w.num_query_tokens), side="right") - 1
+    order = np.random.default_rng(0).permutation(w.num_query_tokens)
+    flops, tokens = 0, 0
+    t0 = time.perf_counter()
+    for first in range(0, len(order), 16):
+        batch = order[first:first + 16]
+        rows = [(int(t), h) for t in batch for h in range(w.num_q_heads)]
+        oracle.prefill(w.q, k, v, w.block_tables, w.context_lens, w.query_start, w.scale,
+                       w.dtype, w.block_size, rows=rows)
+        for t in batch:
+            s = int(seq_of[t])
+            pos = int(w.context_lens[s]) - int(starts[s + 1] - starts[s]) + int(t - starts[s])
+            flops += 4 * w.head_dim * (pos + 1) * w.num_q_heads
+        tokens += len(batch)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"{tokens} of {w.num_query_tokens} query tokens (all {w.num_q_heads} heads) "
+                      f"in {dt:.1f} s, fp64 numpy"}
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return 1
+
+
+def run_prefill(args):
+    """One JSON line for multi-token attention (``pa_prefill``) on a prefill
+    workload: TFLOP/s against the dense bf16 MFMA peak, the oracle beside it."""
+    from paged_kv_cache_310_amd import prefill_bench
+    from paged_kv_cache_310_amd import workloads as wl
+    r = prefill_bench.run(args.prefill_workload, max(args.steps, 1), 0.6)
+    line = {
+        "metric": r["metric"], "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": max(args.steps, 1), "warmup": "0.6 s", "ms_per_step": round(r["us_per_call"] / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": r["workload"], "num_seqs": r["num_seqs"],
+                   "query_tokens": r["query_tokens"], "cached_tokens": r["cached_tokens"],
+                   "heads": r["heads"], "head_dim": 128, "block_size": 16},
+        "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": prefill_bench.PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": r["frac"], "traffic": None,
+                     "kernel": "prefill_kernel"},
+    }
+    if args.cpu_seconds > 0:
+        w = wl.make_prefill_workload(args.prefill_workload, poison=False)
+        line["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -148,6 +214,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.prefill_workload:
+        run_prefill(args)
+        return
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
