@@ -45,6 +45,14 @@ constexpr int kTile = kChunk * kRow;         // 4 KiB
 __device__ __forceinline__ int token_of(int m) { return 4 * (m & 3) + (m >> 2); }
 
 
+// The 16 bytes lane `src` holds (ds_bpermute, one dword at a time).
+__device__ __forceinline__ u32x4 lane_fetch16(const u32x4& v, int src) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)v[j]);
+  return r;
+}
+
 __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
   const uint32_t d = v[e >> 1];
   return (e & 1) ? bf_hi(d) : bf_lo(d);
@@ -55,7 +63,10 @@ __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
 constexpr int kRing = 2;
 
 template <int BS>
-__global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
+// One-wave workgroups; the register budget is set for two waves per SIMD
+// (256 VGPRs, no accumulation registers), so 8 workers can be resident per CU.
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(2)))
+void decode_gqa_kernel(const DecodeArgs a) {
   constexpr int CPB = BS / kChunk;
   static_assert(BS % kChunk == 0, "block size must be a multiple of the chunk");
   const int lane = threadIdx.x;
@@ -105,7 +116,8 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
     u32x4 k[4];            // K operand: token token_of(l%16), dims 32c + 8(l/16)
     u32x4 v[4];            // V rows: load i = token 4i + l/16, dims 8(l%16)..+8
     u32x4 q[4];            // Q^T operand: head l%16, dims 32c + 8(l/16)
-    u32x4 kn[4], vn[4];    // newest token (fused append), valid when meta.slot >= 0
+    u32x4 kn, vn;          // newest token's K/V rows (fused append): lane l holds bytes
+                           // 16 (l%16)..+16, valid when meta.slot >= 0
     ChunkMeta meta;
   };
 
@@ -130,10 +142,8 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
       const size_t row = ((size_t)cur.s * HKV + cur.h) * kRow;
       const __amdgpu_buffer_rsrc_t knr = tile_rsrc(static_cast<const char*>(a.k_new) + row, kRow);
       const __amdgpu_buffer_rsrc_t vnr = tile_rsrc(static_cast<const char*>(a.v_new) + row, kRow);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) t.kn[k] = load16(knr, k * 64 + g4 * 16);   // dims 32k + 8*g4
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t.vn[i] = load16(vnr, g4 * 64 + i * 16);   // dims 32*g4 + 8i
+      t.kn = load16(knr, n * 16);
+      t.vn = load16(vnr, n * 16);
     }
     const int64_t off = (int64_t)next_pb * block_stride + (int64_t)cur.h * BS * kRow +
                         (int64_t)(cur.j % CPB) * kTile;
@@ -215,9 +225,18 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
     // ---- end of this worker's part of the segment
     l = group4_sum(l);   // every lane of head n now holds the head's full sum
     if (mt.slot >= 0) {
+      // Pieces of the newest rows this lane needs, from the lanes of its
+      // group that hold them: K dims 32k + 8 g4 (piece 4k + g4) for the
+      // score, V dims 32 g4 + 8i (piece 4 g4 + i) for the accumulator.
+      const int group_base = lane & 48;
+      u32x4 kq[4], vq[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kq[k] = lane_fetch16(t.kn, group_base + 4 * k + g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vq[i] = lane_fetch16(t.vn, group_base + 4 * g4 + i);
       float d = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d = dot16<uint16_t>(t.q[k], t.kn[k]) + d;
+      for (int k = 0; k < 4; ++k) d = dot16<uint16_t>(t.q[k], kq[k]) + d;
       const float s_new = group4_sum(d) * a.scale_log2;
       const float mm = fmaxf(m, s_new);
       const float al = fast_exp2(m - mm);
@@ -226,21 +245,18 @@ __global__ __launch_bounds__(64, 1) void decode_gqa_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k][i] = fmaf(p, bf16_elem(t.vn[i], k), o[k][i] * al);
+        for (int k = 0; k < 8; ++k) o[k][i] = fmaf(p, bf16_elem(vq[i], k), o[k][i] * al);
       }
       m = mm;
-      // Its K/V rows go to its pool slot: lanes 0, 16, 32, 48 hold every
-      // 16-byte piece of both.
+      // Its K/V rows go to its pool slot: lanes 0..15 hold every 16-byte
+      // piece of both.
       const int64_t blk = mt.slot / BS;
       const int64_t pos = mt.slot - blk * BS;
       const int64_t row_off = ((blk * HKV + mt.h) * BS + pos) * kRow;
       const int f = queue_reserve(q, 2, lane, a.out);
-      if (n == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          queue_put(q, f, k * 64 + g4 * 16, t.kn[k]);
-          queue_put(q, f + 1, g4 * 64 + k * 16, t.vn[k]);
-        }
+      if (g4 == 0) {
+        queue_put(q, f, n * 16, t.kn);
+        queue_put(q, f + 1, n * 16, t.vn);
       }
       queue_job(q, f, static_cast<char*>(a.k_cache) + row_off, kRow, lane);
       queue_job(q, f + 1, static_cast<char*>(a.v_cache) + row_off, kRow, lane);
