@@ -126,16 +126,43 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
 
   // Workgroup ids are dealt round-robin to the 8 XCDs (each with its own
   // L2).  XCD x (ids congruent to x mod 8) takes the (sequence, KV head)
-  // pairs x, x + 8, ..., and each pair's row tiles back to back, heaviest
-  // (last, seeing the most keys under the causal mask) first: the tiles of a
-  // pair run on one XCD at about the same time and share its K/V through
-  // that XCD's L2 instead of each fetching it from HBM.  Dealing pairs
-  // round-robin keeps the XCDs' shares of every sequence equal.
+  // pairs x, x + 8, ...: a pair's tiles run on one XCD and share its K/V
+  // through that XCD's L2 instead of each fetching it from HBM, and dealing
+  // pairs round-robin keeps the XCDs' shares of every sequence equal.  The
+  // order within an XCD follows where the work varies.  Chunks on top of
+  // long earlier contexts cost about the same per tile but differ per pair:
+  // pair by pair, each pair's tiles back to back.  Fresh prompts differ per
+  // tile (a tile's rows see more keys the later they sit): tile level by
+  // tile level, heaviest first, across the XCD's pairs.  Every workgroup
+  // takes the same decision from the batch: causal work (n^2 / 2 per
+  // sequence) against work on the earlier context (n (L - n)).
+  // (Each wave sums over all sequences itself, so no barrier is needed.)
+  float causal_all = 0.f, earlier_all = 0.f;
+  for (int q = lane; q < a.num_seqs; q += 64) {
+    const float nq_s = (float)(a.query_start[q + 1] - a.query_start[q]);
+    causal_all += 0.5f * nq_s * nq_s;
+    earlier_all += nq_s * ((float)a.context_lens[q] - nq_s);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    causal_all += __shfl_xor(causal_all, d);
+    earlier_all += __shfl_xor(earlier_all, d);
+  }
   const int pairs = a.num_seqs * HKV;
+  const int per_xcd = (pairs + kNumXcd - 1) / kNumXcd;
   const int xcd = (int)blockIdx.x % kNumXcd;
-  const int slot = (int)blockIdx.x / kNumXcd;
-  const int pair = (slot / a.tiles_per_seq) * kNumXcd + xcd;
-  const int tile = a.tiles_per_seq - 1 - slot % a.tiles_per_seq;
+  const int slot = (int)blockIdx.x / kNumXcd;   // in [0, tiles_per_seq * per_xcd)
+  int pair, tile;
+  // Equal on every lane (a butterfly gives every lane the same sum); moved
+  // to a scalar so that everything derived from the pair stays scalar.
+  const bool tile_major = uniform(causal_all > earlier_all ? 1 : 0) != 0;
+  if (tile_major) {
+    pair = (slot % per_xcd) * kNumXcd + xcd;
+    tile = a.tiles_per_seq - 1 - slot / per_xcd;
+  } else {
+    pair = (slot / a.tiles_per_seq) * kNumXcd + xcd;
+    tile = a.tiles_per_seq - 1 - slot % a.tiles_per_seq;
+  }
   if (pair >= pairs) return;
   const int s = pair / HKV;
   const int hk = pair % HKV;
