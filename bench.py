@@ -74,6 +74,9 @@ def parse():
     p.add_argument("--prefill-workload", default=None,
                    help="measure multi-token (prefill) attention on this workload instead "
                         "(llama13b_prefill or gqa_chunked_prefill)")
+    p.add_argument("--probe", type=int, default=1,
+                   help="also measure the read ceiling of the same pools with pa_read_probe "
+                        "(0 = skip)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -98,6 +101,65 @@ def counter_traffic(workload: str, kernel: str):
     if not m or not t or m.group(1) != kernel_source_hash(kernel):
         return None
     return float(t.group(1))
+
+
+def decode_tile_order(w) -> np.ndarray:
+    """Tile ids (16-token tiles of a pool, in address order) in the order the
+    decode kernels walk them: KV head by KV head, each sequence's cached
+    tokens in logical order through its block table."""
+    cpb = w.block_size // 16
+    per_head = []
+    for s in range(w.num_seqs):
+        n = -(-int(w.context_lens[s]) // 16)
+        c = np.arange(n)
+        blocks = w.block_tables[s, c // cpb].astype(np.int64)
+        per_head.append(blocks * w.num_kv_heads * cpb + c % cpb)
+    base = np.concatenate(per_head) if per_head else np.zeros(0, np.int64)
+    return np.concatenate([base + h * cpb for h in range(w.num_kv_heads)]).astype(np.int32)
+
+
+def read_ceiling(pa, k, v, w, workers: int, reps: int = 5):
+    """Bandwidth of the decode kernels' access pattern without their
+    arithmetic, measured on the same pools in the same run with
+    pa_read_probe (K plain, V non-temporal, as the attention kernels load
+    them): the tiles the step reads in the decode kernels' own order, every
+    16-token tile of both pools in a random order, and the K pool in address
+    order.  Medians of `reps` timed passes after one untimed."""
+    import torch
+    tile = 16 * w.head_dim * (2 if w.dtype == "bf16" else 4)
+    if tile not in (4096, 8192):
+        return None
+    gen = torch.Generator(device="cpu").manual_seed(3199)
+    ntiles = k.numel() * k.element_size() // tile
+    ids_dec = torch.from_numpy(decode_tile_order(w)).to(k.device)
+    ids_k = torch.randperm(ntiles, generator=gen).to(torch.int32).to(k.device)
+    ids_v = torch.randperm(ntiles, generator=gen).to(torch.int32).to(k.device)
+
+    def timed(fn):
+        fn()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) / 1e3)
+        return float(np.median(out))
+
+    dec = 2 * ids_dec.numel() * tile
+    t_dec = timed(lambda: (pa.pa_read_probe(k, ids_dec, tile, False, num_workers=workers),
+                           pa.pa_read_probe(v, ids_dec, tile, True, num_workers=workers)))
+    both = 2 * ntiles * tile
+    t_rand = timed(lambda: (pa.pa_read_probe(k, ids_k, tile, False, num_workers=workers),
+                            pa.pa_read_probe(v, ids_v, tile, True, num_workers=workers)))
+    t_seq = timed(lambda: pa.pa_read_probe(k, None, tile, False, num_workers=workers))
+    return {"what": f"pa_read_probe, {tile} B tiles, K plain and V non-temporal: the step's "
+                    "tiles in the decode kernels' order; every tile of both pools in random "
+                    f"order; the K pool in address order. {reps} passes, median",
+            "bytes_decode_order": dec, "decode_order_gbps": round(dec / t_dec / 1e9, 1),
+            "bytes_random": both, "random_tiles_gbps": round(both / t_rand / 1e9, 1),
+            "sequential_gbps": round(ntiles * tile / t_seq / 1e9, 1)}
 
 
 def cpu_baseline(w, budget_s: float):
@@ -308,6 +370,8 @@ def main():
         cold_write_ms = float(np.median(cold_write))
         del sweep
 
+    probe = read_ceiling(pa, k, v, w, args.workers) if args.probe else None
+
     kv = w.kv_bytes
     avg_kernel_s = float(kernel_ms.mean()) / 1e3
     achieved = kv / avg_kernel_s / 1e9
@@ -355,6 +419,10 @@ def main():
         "device": torch.cuda.get_device_name(dev),
         "host": platform.node(),
     }
+    if probe is not None:
+        probe["attention_kernel_frac_of_decode_order"] = round(
+            achieved / probe["decode_order_gbps"], 4)
+        result["read_ceiling_probe"] = probe
     if args.cpu_seconds > 0:
         log("timing the CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -208,6 +208,28 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
  * Pass NULL, NULL to stop.  Returns PA_ERR_INVALID if exactly one is NULL. */
 int pa_set_decode_events(void* before, void* after);
 
+/* Read-bandwidth probe (measurement only; not a step of the paged path).
+ * Reads num_tiles tiles of tile_bytes (4096 or 8192) bytes from `base`: tile i
+ * is the one at byte offset tile_ids[i] * tile_bytes, or i * tile_bytes when
+ * tile_ids is NULL.  The reads use the decode kernels' pattern: one-wave
+ * workers, each taking an equal consecutive share of the list, 16-byte loads
+ * (1 KiB per wave load) and 16 KiB in flight per worker; nontemporal = 1
+ * marks every load non-temporal (as the decode kernels mark V).  Timed around
+ * the call, it gives the device's bandwidth for that access pattern -- the
+ * ceiling the attention kernels are compared against.
+ *   checksum    uint32 [workers]: worker w writes the XOR of every 32-bit word
+ *               it read (the XOR over all workers is the XOR of every word of
+ *               every listed tile, each counted once per listing)
+ *   base        device memory of base_bytes bytes, 16-byte aligned
+ *   tile_ids    int32 [num_tiles] or NULL
+ *   num_workers 0 = 4 per compute unit of the current device
+ * Contract: every tile id in [0, base_bytes / tile_bytes) -- checked under
+ * PA_CHECK=1; with tile_ids NULL, num_tiles * tile_bytes <= base_bytes is
+ * checked always.  num_tiles == 0 is a no-op. */
+int pa_read_probe(uint32_t* checksum, const void* base, int64_t base_bytes,
+                  const int32_t* tile_ids, int64_t num_tiles, int tile_bytes, int nontemporal,
+                  int num_workers, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* pa_status_string(int status);
 

@@ -73,6 +73,8 @@ def _load():
         lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i64, i32, i32, i32,
                                    i32, i64, ctypes.c_float, i32, vp]
         lib.pa_prefill.restype = i32
+        lib.pa_read_probe.argtypes = [vp, vp, i64, vp, i64, i32, i32, i32, vp]
+        lib.pa_read_probe.restype = i32
         lib.pa_set_decode_events.argtypes = [vp, vp]
         lib.pa_set_decode_events.restype = i32
         _lib = lib
@@ -222,6 +224,29 @@ def pa_set_decode_events(before=None, after=None) -> None:
 
 
 _workspaces = {}
+
+
+def pa_read_probe(base, tile_ids=None, tile_bytes: int = 4096, nontemporal: bool = False,
+                  num_tiles: Optional[int] = None, num_workers: int = 0,
+                  stream=None) -> torch.Tensor:
+    """Read-bandwidth probe over the bytes of the CUDA tensor ``base``: the
+    tiles ``tile_ids`` (int32, in that order) or, with ``tile_ids=None``, the
+    first ``num_tiles`` tiles in address order (default: every whole tile).
+    Returns the per-worker XOR checksums (int32 tensor on the device)."""
+    _need(base.is_cuda and base.is_contiguous(), "base must be a contiguous CUDA tensor")
+    nbytes = base.numel() * base.element_size()
+    if tile_ids is not None:
+        _need(tile_ids.dtype == torch.int32 and tile_ids.dim() == 1 and tile_ids.is_contiguous()
+              and tile_ids.device == base.device, "tile_ids must be a 1-D int32 tensor on base's device")
+        n = tile_ids.numel()
+    else:
+        n = nbytes // tile_bytes if num_tiles is None else int(num_tiles)
+    workers = num_workers if num_workers > 0 else pa_decode_default_workers()
+    checksum = torch.empty(workers, dtype=torch.int32, device=base.device)
+    _call("pa_read_probe", _load().pa_read_probe(
+        _ptr(checksum), _ptr(base), nbytes, _ptr(tile_ids), n, int(tile_bytes),
+        1 if nontemporal else 0, workers, _stream(base.device, stream)))
+    return checksum
 
 
 def decode_workspace(device, nbytes: int) -> torch.Tensor:

@@ -139,6 +139,45 @@ int pa_set_decode_events(void* before, void* after) {
   return PA_OK;
 }
 
+}  // extern "C"
+
+namespace pa {
+// Read-bandwidth probe (probe_kernel.hip): tile_bytes 4096 or 8192.
+hipError_t launch_read_probe(uint32_t* checksum, const void* base, const int32_t* tile_ids,
+                             int64_t num_tiles, int tile_bytes, int nontemporal, int workers,
+                             hipStream_t stream);
+}  // namespace pa
+
+extern "C" {
+
+int pa_read_probe(uint32_t* checksum, const void* base, int64_t base_bytes,
+                  const int32_t* tile_ids, int64_t num_tiles, int tile_bytes, int nontemporal,
+                  int num_workers, void* stream) {
+  if (num_tiles < 0 || base_bytes < 0 || num_workers < 0 ||
+      (tile_bytes != 4096 && tile_bytes != 8192) || (nontemporal != 0 && nontemporal != 1))
+    return PA_ERR_INVALID;
+  if (num_tiles == 0) return PA_OK;
+  if (!checksum || !base || !aligned16(base)) return PA_ERR_INVALID;
+  const int64_t tiles_in_base = base_bytes / tile_bytes;
+  if (tile_ids == nullptr && num_tiles > tiles_in_base) return PA_ERR_INVALID;
+  int workers = num_workers;
+  if (workers == 0) {
+    const int st = default_workers_for_current_device(&workers);
+    if (st != PA_OK) return st;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (tile_ids != nullptr && check_enabled()) {
+    std::vector<int32_t> ids;
+    if (!copy_to_host(ids, tile_ids, (size_t)num_tiles, st)) return PA_ERR_HIP;
+    for (int32_t id : ids)
+      if (id < 0 || id >= tiles_in_base) return PA_ERR_INDEX;
+  }
+  return pa::launch_read_probe(checksum, base, tile_ids, num_tiles, tile_bytes, nontemporal,
+                               workers, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
 const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";

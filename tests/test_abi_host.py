@@ -169,3 +169,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _binding._load()
+
+
+def test_read_probe_rejects_bad_arguments_before_any_hip_call(lib):
+    def st(checksum=FAKE, base=FAKE, base_bytes=1 << 20, ids=None, n=16, tile=4096, nt=0, w=8):
+        return lib.pa_read_probe(checksum, base, base_bytes, ids, n, tile, nt, w, None)
+    assert st(tile=1024) == 1
+    assert st(tile=16384) == 1
+    assert st(nt=2) == 1
+    assert st(n=-1) == 1
+    assert st(w=-1) == 1
+    assert st(base_bytes=-1) == 1
+    assert st(checksum=None) == 1
+    assert st(base=None) == 1
+    assert st(base=FAKE + 8) == 1                       # not 16-byte aligned
+    assert st(n=(1 << 20) // 4096 + 1) == 1              # more tiles than the buffer holds
+    assert st(n=0, checksum=None, base=None) == 0        # nothing to do

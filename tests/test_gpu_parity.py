@@ -255,12 +255,14 @@ print(status(lambda: pa.pa_decode(q, k, v, tab, torch.tensor([20, 3], dtype=torc
       k_new=kn, v_new=vn, slot_mapping=torch.tensor([1 * 16 + 3, 2 * 16 + 2], device=d))))
 print(status(lambda: pa.pa_decode(q, k, v, tab, torch.tensor([20, 3], dtype=torch.int32, device=d), 0.125,
       k_new=kn, v_new=vn, slot_mapping=torch.tensor([1 * 16 + 3, -1], device=d))))
+print(status(lambda: pa.pa_read_probe(k, torch.tensor([0, 16], dtype=torch.int32, device=d))))
+print(status(lambda: pa.pa_read_probe(k, torch.tensor([0, 15], dtype=torch.int32, device=d))))
 """
     env = dict(os.environ, PA_CHECK="1")
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
                          timeout=120, cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert res.returncode == 0, res.stderr
-    assert res.stdout.split() == ["5", "5", "5", "5", "5", "0", "0"], res.stdout
+    assert res.stdout.split() == ["5", "5", "5", "5", "5", "0", "0", "5", "0"], res.stdout
 
 
 # ---------------------------------------------------------- full-size workloads
