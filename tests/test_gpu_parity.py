@@ -149,6 +149,26 @@ def test_empty_sequences_give_zero_rows():
     assert torch.count_nonzero(out0).item() == 0
 
 
+@pytest.mark.parametrize("hq,hkv,append", [(2, 2, True), (8, 1, True), (2, 2, False)],
+                         ids=["mha-append", "gqa8-append", "mha-with-empty"])
+def test_more_sequences_than_the_length_cache(hq, hkv, append):
+    """5,000 sequences: the split caches 4,096 lengths in LDS and reads the
+    rest from memory; ragged 0..40-token contexts, many segments per worker."""
+    rng = np.random.default_rng(4242 + hq)
+    lens = rng.integers(1 if append else 0, 41, 5000)
+    say("many sequences", hq, hkv, append, int(lens.sum()), "tokens")
+    w = small(wl.BF16, 128, 16, hq, hkv, lens=lens.tolist(), append=append, seed=21 + hq)
+    out = DeviceWorkload(w).step()
+    got = out_f64(out)
+    assert not np.isnan(got).any()
+    if not append:
+        assert np.all(got[lens == 0] == 0)
+    rows = sample_rows(w, per_seq_heads=1, seed=3)
+    k, v = oracle_pools(w)
+    err = assert_attention_close(got, oracle_decode(w, k, v, rows=rows), wl.BF16, rows=rows)
+    say("max-abs %.3e row-rel %.3e" % err)
+
+
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.FP32])
 def test_single_token_returns_its_value_exactly(dtype):
     w = small(dtype, 128 if dtype == wl.BF16 else 64, 16, 4, 4, lens=[1] * 9, append=True, seed=16)
