@@ -106,6 +106,19 @@ __device__ __forceinline__ uint64_t lds_read_tr16(const char* base, int offset) 
   return __builtin_bit_cast(uint64_t, v);
 }
 
+// Maximum of scores straight from the matrix cores.  The scores are finite
+// or -inf (masked keys), so the NaN-propagating maximum gives fmaxf's value,
+// and it maps to v_maximum3_f32 without the quieting copies fmaxf needs on
+// values the compiler cannot prove canonical.
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// Maximum over the four lanes that share l%16 (two permlane swaps).
+__device__ __forceinline__ float group4_smax(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = smax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return smax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // (1, 1) in bf16, for pair sums with v_dot2_f32_bf16.
 __device__ constexpr bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
@@ -366,9 +379,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
             for (int i = 0; i < 4; ++i)
               if (k0 + 16 * half + 4 * g4 + i > pos[rt]) x[4 * half + i] = -INFINITY;
         }
-        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mx = group4_max(mx);
+        float mx = smax(smax(smax(x[0], x[1]), smax(x[2], x[3])),
+                        smax(smax(x[4], x[5]), smax(x[6], x[7])));
+        mx = group4_smax(mx);
         // Tile max in the exp2 domain (cexp >= 0 keeps the order).
         mx = mx == -INFINITY ? -INFINITY : mx * cexp;
         const bool grow = mx > m_run[rt] + kRescaleSlack;
