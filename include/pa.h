@@ -43,6 +43,10 @@
  *    behaviour.  With the environment variable PA_CHECK=1 every call copies
  *    its index arrays to the host, synchronising `stream`, and returns
  *    PA_ERR_INDEX instead of launching when they break the contract.
+ *  - Without PA_CHECK a call only launches kernels on `stream`, so a sequence
+ *    of calls can be captured in a HIP graph and replayed, provided the
+ *    caller allocates the workspace and outputs beforehand.  Under PA_CHECK=1
+ *    a call copies to the host and synchronizes, and cannot be captured.
  *  - The library never prints, throws or aborts.
  */
 #ifndef PA_H
