@@ -163,8 +163,14 @@ int pa_decode_default_workers(int* num_workers);
  *     pa_decode without them.  Contract: slot_mapping[s] is negative or the
  *     slot of position context_lens[s]-1 of sequence s.
  *   workspace      see pa_decode_workspace_size (read/written)
- *   num_workers    0 = default; otherwise the exact number of workers, a
- *                  tuning knob that changes only the fp32 summation order.
+ *   num_workers    0 = default: every worker resident at once (4 per
+ *                  compute unit), but at most 48 per segment -- a (sequence,
+ *                  KV head) pair on the matrix-core kernel, a (sequence,
+ *                  query head) pair otherwise -- rounded up to a multiple of
+ *                  8, so that small batches do not spend more time merging
+ *                  split pieces than they gain; otherwise the exact number of
+ *                  workers.  A tuning knob that changes only the fp32
+ *                  summation order.
  * Contract: 0 <= context_lens[s] <= max_blocks_per_seq * block_size; table
  * entries for the blocks a sequence uses lie in [0, num_blocks); entries past
  * them are never read. */
