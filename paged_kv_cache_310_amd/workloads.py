@@ -28,6 +28,9 @@ shared_prefix_fork     same groups forked at 1024 + U[1,15] tokens: the
 gqa_pareto_bs16/32     256 seqs, 64 query heads over 8 KV heads, d 128,
                        bf16, Pareto(alpha 1.2, x_m 128) lengths capped at
                        32768, pool 1.25x need, 1-token append
+gqa_single_4k/32k      one sequence, 64/8 heads, d 128, bs 16, bf16, 4096 or
+                       32768 tokens after a 1-token append, pool 1.25x need
+                       (the latency regime: one segment per KV head)
 =====================  =====================================================
 
 Draw order per workload (one ``numpy.random.default_rng(seed)``): lengths,
@@ -264,7 +267,8 @@ def _pareto_lengths(rng, n):
 
 
 WORKLOADS = ("tiny_fp32", "opt13b_mha", "llama13b_long", "shared_prefix_steady",
-             "shared_prefix_fork", "gqa_pareto_bs16", "gqa_pareto_bs32")
+             "shared_prefix_fork", "gqa_pareto_bs16", "gqa_pareto_bs32", "gqa_single_4k",
+             "gqa_single_32k")
 
 
 def make_workload(name: str, poison: bool = True) -> Workload:
@@ -294,6 +298,10 @@ def make_workload(name: str, poison: bool = True) -> Workload:
         bs = 16 if name.endswith("16") else 32
         return make_simple(name, 3105, BF16, 64, 8, 128, bs, lens, append=True, poison=poison,
                            max_len=32768, rng=rng)
+    if name in ("gqa_single_4k", "gqa_single_32k"):
+        n = 4096 if name.endswith("4k") else 32768
+        return make_simple(name, 3106, BF16, 64, 8, 128, 16, [n], append=True, poison=poison,
+                           rng=np.random.default_rng(3106))
     raise KeyError(f"unknown workload {name!r}; choose from {WORKLOADS}")
 
 
@@ -311,6 +319,8 @@ def workload_lengths(name: str) -> np.ndarray:
         return np.repeat(1024 + np.random.default_rng(3104).integers(1, 16, 16), 8) + 1
     if name in ("gqa_pareto_bs16", "gqa_pareto_bs32"):
         return _pareto_lengths(np.random.default_rng(3105), 256)
+    if name in ("gqa_single_4k", "gqa_single_32k"):
+        return np.array([4096 if name.endswith("4k") else 32768])
     raise KeyError(name)
 
 

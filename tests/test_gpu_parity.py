@@ -350,3 +350,11 @@ def test_workload_gqa_pareto(cache, name):
     longest = np.argsort(w.context_lens)[-2:]
     rows = sample_rows(w) + [(int(s), h) for s in longest for h in range(w.num_q_heads)]
     _check_full(w, rows=sorted(set(rows)))
+
+
+@pytest.mark.parametrize("name", ["gqa_single_4k", "gqa_single_32k"])
+def test_workload_gqa_single_sequence(cache, name):
+    """One sequence: each KV head's segment is split over many workers and
+    merged (the default worker count is capped per segment)."""
+    w = _full(cache, name)
+    _check_full(w, rows=[(0, h) for h in range(w.num_q_heads)])
