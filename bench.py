@@ -73,7 +73,7 @@ def parse():
                    help="CPU oracle time budget for the baseline sample (0 = skip)")
     p.add_argument("--prefill-workload", default=None,
                    help="measure multi-token (prefill) attention on this workload instead "
-                        "(llama13b_prefill or gqa_chunked_prefill)")
+                        "(llama13b_prefill, gqa_chunked_prefill or gqa_single_chunk_32k)")
     p.add_argument("--probe", type=int, default=1,
                    help="also measure the read ceiling of the same pools with pa_read_probe "
                         "(0 = skip)")
@@ -257,7 +257,8 @@ def run_prefill(args):
         "data": "synthetic",
         "config": {"workload": r["workload"], "num_seqs": r["num_seqs"],
                    "query_tokens": r["query_tokens"], "cached_tokens": r["cached_tokens"],
-                   "heads": r["heads"], "head_dim": 128, "block_size": 16},
+                   "heads": r["heads"], "head_dim": 128, "block_size": 16,
+                   "context_splits": r["context_splits"]},
         "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": prefill_bench.PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": r["frac"], "traffic": None,
                      "kernel": "prefill_kernel"},

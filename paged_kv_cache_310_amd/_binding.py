@@ -73,6 +73,12 @@ def _load():
         lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i64, i32, i32, i32,
                                    i32, i64, ctypes.c_float, i32, vp]
         lib.pa_prefill.restype = i32
+        lib.pa_prefill_split.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i64, i32, i32,
+                                         i32, i32, i64, ctypes.c_float, i32, i32, vp, sz, vp]
+        lib.pa_prefill_split.restype = i32
+        lib.pa_prefill_split_plan.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32,
+                                              ctypes.POINTER(i32), ctypes.POINTER(sz)]
+        lib.pa_prefill_split_plan.restype = i32
         lib.pa_read_probe.argtypes = [vp, vp, i64, vp, i64, i32, i32, i32, vp]
         lib.pa_read_probe.restype = i32
         lib.pa_set_decode_events.argtypes = [vp, vp]
@@ -298,13 +304,28 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
     return out
 
 
+def pa_prefill_split_plan(num_seqs: int, max_query_len: int, num_query_tokens: int,
+                          num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                          max_blocks_per_seq: int, num_splits: int = 0):
+    """(splits, workspace bytes) that ``pa_prefill(..., num_splits=...)`` uses
+    for these sizes; ``num_splits`` 0 asks for the automatic choice."""
+    splits, nbytes = ctypes.c_int(0), ctypes.c_size_t(0)
+    _call("pa_prefill_split_plan", _load().pa_prefill_split_plan(
+        num_seqs, max_query_len, num_query_tokens, num_q_heads, num_kv_heads, head_dim,
+        block_size, max_blocks_per_seq, num_splits, ctypes.byref(splits), ctypes.byref(nbytes)))
+    return int(splits.value), int(nbytes.value)
+
+
 def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
-               max_query_len: Optional[int] = None, out=None, stream=None) -> torch.Tensor:
+               max_query_len: Optional[int] = None, out=None, stream=None, num_splits: int = 1,
+               workspace=None) -> torch.Tensor:
     """Causal attention of each sequence's query chunk (its newest tokens,
     already appended) through the block table; returns ``out``
     [num_query_tokens, num_q_heads, head_dim].  ``max_query_len`` bounds every
     chunk; when omitted it is read from ``query_start`` (a device-to-host
-    copy)."""
+    copy).  ``num_splits`` other than 1 shares each row tile's keys out over
+    that many workgroups (0: the library's choice) through ``pa_prefill_split``;
+    ``workspace`` (a uint8 device tensor) is then allocated when not given."""
     nb, hkv, bs, d = _check_cache(k_cache, v_cache)
     _need(q.dim() == 3 and q.shape[2] == d and q.dtype == k_cache.dtype and q.is_contiguous()
           and q.device == k_cache.device,
@@ -326,8 +347,21 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, sca
         out = torch.empty_like(q)
     _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
           and out.device == q.device, "out must match q")
-    _call("pa_prefill", _load().pa_prefill(
+    if num_splits == 1:
+        _call("pa_prefill", _load().pa_prefill(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), _ptr(query_start), b, int(max_query_len),
+            t, hq, hkv, d, bs, nb, float(scale), _dtype_code(q), _stream(q.device, stream)))
+        return out
+    if workspace is None:
+        _, nbytes = pa_prefill_split_plan(b, int(max_query_len), t, hq, hkv, d, bs,
+                                          block_tables.shape[1], int(num_splits))
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace.is_cuda and workspace.is_contiguous() and workspace.device == q.device,
+          "workspace must be a contiguous device tensor on q's device")
+    _call("pa_prefill_split", _load().pa_prefill_split(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(query_start), b, int(max_query_len), t,
-        hq, hkv, d, bs, nb, float(scale), _dtype_code(q), _stream(q.device, stream)))
+        hq, hkv, d, bs, nb, float(scale), _dtype_code(q), int(num_splits), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q.device, stream)))
     return out

@@ -412,13 +412,72 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
              : PA_ERR_HIP;
 }
 
-int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
-               const int32_t* block_tables, int max_blocks_per_seq,
-               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
-               int max_query_len, int64_t num_query_tokens, int num_q_heads, int num_kv_heads,
-               int head_dim, int block_size, int64_t num_blocks, float scale, int dtype,
-               void* stream) {
+}  // extern "C"
+
+namespace pa {
+// Prefill with the context split over num_splits workgroups per row tile
+// (prefill_kernel.hip).  partials may be null when num_splits is 1.
+hipError_t launch_prefill_split(const PrefillArgs& a, int block_size, int num_splits,
+                                float* partials, int64_t num_query_tokens, hipStream_t stream);
+}  // namespace pa
+
+namespace {
+
+constexpr int kPrefillMaxSplits = 16;
+constexpr int kPrefillWgsPerCu = 3;        // resident prefill workgroups per CU
+constexpr int kPrefillMinStepsPerSplit = 16;
+
+// Splits pa_prefill_split picks for num_splits = 0.  None while the row tiles
+// alone fill the device's workgroup slots (3 per compute unit) twice.
+// Otherwise S in [2, Smax], Smax = floor(2 slots / tiles) (at least 2, at most
+// 16, and at most one split per 16 key steps of the longest context the
+// tables allow), with the smallest per-CU share ceil(tiles S / CUs) / S of one
+// tile's work -- splits that leave some CUs a workgroup more than others lose
+// -- and among equal shares the most splits (more resident workgroups).
+int prefill_auto_splits(int num_seqs, int max_query_len, int group, int num_kv_heads,
+                        int max_blocks_per_seq, int block_size, int* splits) {
+  int cus = 0;
+  const int st = current_device_cus(&cus);
+  if (st != PA_OK) return st;
+  const int64_t tiles =
+      ((int64_t)max_query_len * group + pa::kPrefillRowsPerWg - 1) / pa::kPrefillRowsPerWg;
+  const int64_t wgs = tiles * num_seqs * num_kv_heads;
+  const int64_t slots = (int64_t)cus * kPrefillWgsPerCu;
+  const int64_t max_steps = ((int64_t)max_blocks_per_seq * block_size + 31) / 32;
+  int64_t best = 1;
+  if (wgs > 0 && wgs < 2 * slots) {
+    int64_t smax = 2 * slots / wgs;
+    smax = smax > 2 ? smax : 2;
+    smax = smax < kPrefillMaxSplits ? smax : kPrefillMaxSplits;
+    const int64_t by_steps = max_steps / kPrefillMinStepsPerSplit;
+    smax = smax < by_steps ? smax : by_steps;
+    int64_t best_load = 0;
+    for (int64_t n = 2; n <= smax; ++n) {
+      const int64_t load = (wgs * n + cus - 1) / cus;   // workgroups on the busiest CU
+      // load / n <= best_load / best, exactly
+      if (best == 1 || load * best <= best_load * n) {
+        best = n;
+        best_load = load;
+      }
+    }
+  }
+  *splits = (int)best;
+  return PA_OK;
+}
+
+size_t prefill_partials_bytes(int splits, int64_t num_query_tokens, int num_q_heads,
+                              int head_dim) {
+  return splits > 1 ? (size_t)splits * num_query_tokens * num_q_heads * (head_dim + 4) * 4 : 0;
+}
+
+int prefill_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, int max_blocks_per_seq,
+                 const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                 int max_query_len, int64_t num_query_tokens, int num_q_heads, int num_kv_heads,
+                 int head_dim, int block_size, int64_t num_blocks, float scale, int dtype,
+                 int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_query_len < 0 || num_query_tokens < 0 ||
+      num_splits < 0 || num_splits > kPrefillMaxSplits ||
       num_q_heads <= 0 || !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks) ||
       num_q_heads % num_kv_heads != 0 || !(scale == scale))
     return PA_ERR_INVALID;
@@ -436,6 +495,18 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   const int64_t pair_rounds = ((int64_t)num_seqs * num_kv_heads + pa::kNumXcd - 1) / pa::kNumXcd;
   if (tiles * pa::kNumXcd * pair_rounds > INT32_MAX || num_query_tokens * num_q_heads > INT32_MAX)
     return PA_ERR_UNSUPPORTED;
+
+  if (num_splits == 0) {
+    const int sp = prefill_auto_splits(num_seqs, max_query_len, group, num_kv_heads,
+                                       max_blocks_per_seq, block_size, &num_splits);
+    if (sp != PA_OK) return sp;
+  }
+  if (tiles * pa::kNumXcd * pair_rounds * num_splits > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_splits > 1) {
+    const size_t need = prefill_partials_bytes(num_splits, num_query_tokens, num_q_heads,
+                                               head_dim);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+  }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (check_enabled()) {
@@ -473,7 +544,59 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   a.group = group;
   a.tiles_per_seq = (int)tiles;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return pa::launch_prefill(a, block_size, st) == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return pa::launch_prefill_split(a, block_size, num_splits, static_cast<float*>(workspace),
+                                  num_query_tokens, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, int max_blocks_per_seq,
+               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+               int max_query_len, int64_t num_query_tokens, int num_q_heads, int num_kv_heads,
+               int head_dim, int block_size, int64_t num_blocks, float scale, int dtype,
+               void* stream) {
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                      query_start, num_seqs, max_query_len, num_query_tokens, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, 1, nullptr, 0,
+                      stream);
+}
+
+int pa_prefill_split_plan(int num_seqs, int max_query_len, int64_t num_query_tokens,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int max_blocks_per_seq, int num_splits, int* splits, size_t* bytes) {
+  if (!splits || !bytes || num_seqs < 0 || max_query_len < 0 || num_query_tokens < 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads != 0 || num_splits < 0 ||
+      num_splits > kPrefillMaxSplits)
+    return PA_ERR_INVALID;
+  int n = num_splits;
+  if (n == 0) {
+    const int st = prefill_auto_splits(num_seqs, max_query_len, num_q_heads / num_kv_heads,
+                                       num_kv_heads, max_blocks_per_seq, block_size, &n);
+    if (st != PA_OK) return st;
+  }
+  *splits = n;
+  *bytes = prefill_partials_bytes(n, num_query_tokens, num_q_heads, head_dim);
+  return PA_OK;
+}
+
+int pa_prefill_split(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                     int max_query_len, int64_t num_query_tokens, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                     float scale, int dtype, int num_splits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                      query_start, num_seqs, max_query_len, num_query_tokens, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, num_splits,
+                      workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -127,10 +127,25 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-template <int BS>
+// Context split: the key steps of every row tile are shared out over
+// num_splits workgroups, which write unnormalized partial rows (acc[D],
+// reference max, sum) to `partials` for prefill_merge_kernel.  num_splits 1:
+// each workgroup walks all its keys and writes `out` directly.
+struct SplitArgs {
+  int num_splits;
+  float* partials;              // [num_splits][num_query_tokens][num_q_heads][kPartRow]
+  int64_t num_query_tokens;
+};
+constexpr int kPartRow = kPD + 4;   // acc[128], max, sum, 2 floats of padding
+
+// kSplit: the workgroup takes one split of its row tile's key steps and
+// writes partial rows (compiled apart, so the unsplit kernel keeps its
+// registers).
+template <int BS, bool kSplit>
 // Three workgroups (12 waves) per CU: the register budget this sets (168)
 // costs a few spilled registers and measured faster than two workgroups.
-__global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs a,
+                                                               const SplitArgs sp) {
   __shared__ __attribute__((aligned(16))) char lds[kBufs][kBufBytes];
   __shared__ int32_t tab[kTableCap];
   const int tid = threadIdx.x;
@@ -169,7 +184,10 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   const int pairs = a.num_seqs * HKV;
   const int per_xcd = (pairs + kNumXcd - 1) / kNumXcd;
   const int xcd = (int)blockIdx.x % kNumXcd;
-  const int slot = (int)blockIdx.x / kNumXcd;   // in [0, tiles_per_seq * per_xcd)
+  // The splits of one row tile are consecutive workgroups of one XCD.
+  const int num_splits = kSplit ? sp.num_splits : 1;
+  const int split = ((int)blockIdx.x / kNumXcd) % num_splits;
+  const int slot = (int)blockIdx.x / kNumXcd / num_splits;   // in [0, tiles_per_seq * per_xcd)
   int pair, tile;
   // Equal on every lane (a butterfly gives every lane the same sum); moved
   // to a scalar so that everything derived from the pair stays scalar.
@@ -193,6 +211,10 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   const int last_row = min(row0 + kPrefillRowsPerWg, rows) - 1;
   const int p_max = L - nq + last_row / G;       // highest position a row here has
   const int steps = p_max / kKeys + 1;
+  // This workgroup's share of the key steps (all of them without a split).
+  const int split_steps = (steps + num_splits - 1) / num_splits;
+  const int t_begin = kSplit ? min(steps, split * split_steps) : 0;
+  const int t_end = kSplit ? min(steps, t_begin + split_steps) : steps;
 
   // Row tile rt of wave w covers rows row0 + 16 (rt kWaves + w) .. +16: the
   // waves' tiles interleave, so under the causal mask the waves of a
@@ -241,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
       tab[i] = table[first + i];
   };
   constexpr int kStepsPerTable = kTableCap * BS / kKeys;
-  stage_table(0);
+  if (!kSplit || t_begin < t_end) stage_table(t_begin / kStepsPerTable * kTableCap);
   __syncthreads();
 
   // Step loads: thread tid moves key tid/16 + (kThreads/16) h of the step,
@@ -297,15 +319,32 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   // Step j's rows travel in register slot j % kDepth and LDS buffer
   // j % kBufs.  The slot is free again once step j is stashed, the buffer
   // once step j is computed (kBufs - 1 iterations before it is refilled).
+  if constexpr (kSplit) {
+    // A split may start anywhere in a table window, so the first kDepth
+    // steps can reach into the next one: restage it there, as the loop does.
 #pragma unroll
-  for (int j = 0; j < kDepth; ++j)
-    if (j < steps) fetch(j * kKeys, j);
-  stash(0, 0);
+    for (int j = 0; j < kDepth; ++j) {
+      const int tj = t_begin + j;
+      if (tj >= t_end) break;
+      if (j > 0 && tj % kStepsPerTable == 0) {
+        __syncthreads();
+        stage_table(tj / kStepsPerTable * kTableCap);
+        __syncthreads();
+      }
+      fetch(tj * kKeys, tj % kDepth);
+    }
+    if (t_begin < t_end) stash(t_begin % kDepth, t_begin % kBufs);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j)
+      if (j < steps) fetch(j * kKeys, j);
+    stash(0, 0);
+  }
   __syncthreads();
-  for (int t = 0; t < steps; ++t) {
+  for (int t = t_begin; t < t_end; ++t) {
     const int k0 = t * kKeys;
     const int ahead = t + kDepth;
-    if (ahead < steps) {
+    if (ahead < t_end) {
       if (ahead % kStepsPerTable == 0) {
         // Step `ahead` needs the next table window; every fetch of the
         // current one has been issued, so refill it between two barriers.
@@ -387,7 +426,10 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
         const bool grow = mx > m_run[rt] + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(grow)) {
           const float m_new = grow ? mx : m_run[rt];
-          const float alpha = fast_exp2(m_run[rt] - m_new);   // 1 where the reference stays
+          // 1 where the reference stays (also for a row still at m = -inf,
+          // where the difference would be NaN).
+          const float alpha =
+              !kSplit || grow ? fast_exp2(m_run[rt] - m_new) : 1.f;
           m_run[rt] = m_new;
           l_run[rt] *= alpha;
 #pragma unroll
@@ -396,7 +438,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
         // Weights 2^(cexp x - m), rounded to bf16; the running sum adds the
         // rounded pairs with one dot product each.
         uint32_t pb[4];
-        const float neg_m = -m_run[rt];
+        // A row that has seen no key yet (possible only in a later split)
+        // keeps m = -inf: its weights are then 2^-inf = 0.
+        const float neg_m = kSplit && m_run[rt] == -INFINITY ? 0.f : -m_run[rt];
         // x = -inf gives 2^-inf = 0 for cexp > 0; with cexp == 0 the product
         // would be NaN, so masked weights are zeroed explicitly then.
         float w[8];
@@ -424,8 +468,28 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
               acc[rt][c], 0, 0, 0);
       }
     }
-    if (t + 1 < steps) stash((t + 1) % kDepth, (t + 1) % kBufs);
+    if (t + 1 < t_end) stash((t + 1) % kDepth, (t + 1) % kBufs);
     __syncthreads();
+  }
+
+  if constexpr (kSplit) {
+    // Unnormalized partial row for the merge: acc relative to the row's
+    // reference max, the max and the sum.
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      const float total = group4_sum(l_run[rt]);
+      const int r = tile_row0(rt) + n;
+      if (r >= rows) continue;
+      float* prow = sp.partials +
+                    (((int64_t)split * sp.num_query_tokens + q0 + r / G) * HQ + hk * G + r % G) *
+                        kPartRow;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<float4*>(prow + 16 * c + 4 * g4) =
+            make_float4(acc[rt][c][0], acc[rt][c][1], acc[rt][c][2], acc[rt][c][3]);
+      if (g4 == 0) *reinterpret_cast<float2*>(prow + kPD) = make_float2(m_run[rt], total);
+    }
+    return;
   }
 
   // Normalise and store: lane l holds dims 16c + 4g + i (i = 0..3) of its
@@ -447,23 +511,78 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   }
 }
 
+// Folds the num_splits partial rows of every (query token, query head) row
+// into `out`: with M the largest reference max, out = sum_s acc_s 2^(m_s - M)
+// / sum_s l_s 2^(m_s - M).  Splits that saw no key of the row carry
+// m = -inf and add nothing; the first split always holds key 0, which every
+// row sees.  Four waves of two rows each per workgroup, four dims per lane.
+constexpr int kMergeRowsPerWg = 8;
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a,
+                                                            const SplitArgs sp) {
+  const int64_t rows = sp.num_query_tokens * a.num_q_heads;
+  const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerWg + threadIdx.x / 32;
+  if (row >= rows) return;
+  const int d0 = (threadIdx.x % 32) * 4;
+  const int64_t split_stride = rows * kPartRow;
+  const float* base = sp.partials + row * kPartRow;
+  float M = -INFINITY;
+  for (int s = 0; s < sp.num_splits; ++s) M = fmaxf(M, base[s * split_stride + kPD]);
+  float S = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < sp.num_splits; ++s) {
+    const float* p = base + s * split_stride;
+    const float2 ml = *reinterpret_cast<const float2*>(p + kPD);
+    const float f = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
+    const float4 o = *reinterpret_cast<const float4*>(p + d0);
+    S = fmaf(ml.y, f, S);
+    O[0] = fmaf(o.x, f, O[0]);
+    O[1] = fmaf(o.y, f, O[1]);
+    O[2] = fmaf(o.z, f, O[2]);
+    O[3] = fmaf(o.w, f, O[3]);
+  }
+  const float inv = 1.f / S;
+  *reinterpret_cast<uint2*>(static_cast<char*>(a.out) + (row * kPD + d0) * 2) =
+      make_uint2(cvt_bf16x2(O[0] * inv, O[1] * inv), cvt_bf16x2(O[2] * inv, O[3] * inv));
+}
+
 }  // namespace
 
 bool prefill_supported(int dtype, int head_dim, int block_size) {
   return dtype == kBf16 && head_dim == kPD && (block_size == 16 || block_size == 32);
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int block_size, hipStream_t stream) {
+// Declared where it is called (pa_api.hip).  partials may be null when
+// num_splits is 1.
+hipError_t launch_prefill_split(const PrefillArgs& a, int block_size, int num_splits,
+                                float* partials, int64_t num_query_tokens, hipStream_t stream) {
   // Whole rounds of 8 pairs: workgroups past the last pair leave at once.
-  const int64_t blocks =
-      (int64_t)a.tiles_per_seq * kNumXcd * ((a.num_seqs * a.num_kv_heads + kNumXcd - 1) / kNumXcd);
+  const int64_t blocks = (int64_t)a.tiles_per_seq * kNumXcd *
+                         ((a.num_seqs * a.num_kv_heads + kNumXcd - 1) / kNumXcd) * num_splits;
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  if (block_size == 16)
-    hipLaunchKernelGGL(prefill_kernel<16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<32>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  const SplitArgs sp{num_splits, partials, num_query_tokens};
+  const dim3 grid((unsigned)blocks), wg(kThreads);
+  if (num_splits == 1) {
+    if (block_size == 16)
+      hipLaunchKernelGGL((prefill_kernel<16, false>), grid, wg, 0, stream, a, sp);
+    else
+      hipLaunchKernelGGL((prefill_kernel<32, false>), grid, wg, 0, stream, a, sp);
+  } else {
+    if (block_size == 16)
+      hipLaunchKernelGGL((prefill_kernel<16, true>), grid, wg, 0, stream, a, sp);
+    else
+      hipLaunchKernelGGL((prefill_kernel<32, true>), grid, wg, 0, stream, a, sp);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || num_splits == 1) return e;
+  const int64_t rows = num_query_tokens * a.num_q_heads;
+  const int64_t wgs = (rows + kMergeRowsPerWg - 1) / kMergeRowsPerWg;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a, sp);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int block_size, hipStream_t stream) {
+  return launch_prefill_split(a, block_size, 1, nullptr, 0, stream);
 }
 
 }  // namespace pa

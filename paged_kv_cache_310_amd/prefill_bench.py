@@ -3,7 +3,10 @@ paged_kv_cache_310_amd.prefill_bench [--workload NAME]`` prints one JSON line
 per workload.
 
 The timed call is ``pa_prefill`` alone (the chunk's append runs once before
-timing); inputs are resident in HBM.  Device time comes from HIP events on
+timing) with the library's automatic context split (``num_splits=0``: no
+split unless the batch's row tiles leave the device underfilled; then the
+split kernel and the merge of the split rows are both timed); inputs are
+resident in HBM.  Device time comes from HIP events on
 the stream the call uses, averaged over ``--iters`` calls after at least
 ``--warmup-s`` seconds of untimed calls.  Algorithmic work: every query row
 (query token x query head) at position p costs 4 * head_dim * (p + 1) flops
@@ -53,9 +56,14 @@ def run(name: str, iters: int, warmup_s: float) -> dict:
     lens, qs = to_dev(w.context_lens), to_dev(w.query_start)
     out = torch.empty_like(q)
     mq = w.max_query_len
+    splits, nbytes = pa.pa_prefill_split_plan(w.num_seqs, mq, w.num_query_tokens, w.num_q_heads,
+                                              w.num_kv_heads, w.head_dim, w.block_size,
+                                              w.block_tables.shape[1], 0)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
 
     def call():
-        pa.pa_prefill(q, k, v, tab, lens, qs, float(w.scale), max_query_len=mq, out=out)
+        pa.pa_prefill(q, k, v, tab, lens, qs, float(w.scale), max_query_len=mq, out=out,
+                      num_splits=0, workspace=ws)
 
     t_end = time.perf_counter() + warmup_s
     while time.perf_counter() < t_end:
@@ -75,7 +83,7 @@ def run(name: str, iters: int, warmup_s: float) -> dict:
         "metric": "paged prefill attention: achieved TFLOP/s (bf16 matrix cores)",
         "workload": name, "num_seqs": w.num_seqs, "query_tokens": w.num_query_tokens,
         "cached_tokens": int(w.context_lens.sum()), "heads": [w.num_q_heads, w.num_kv_heads],
-        "us_per_call": round(us, 2), "algorithmic_flops": flops,
+        "context_splits": splits, "us_per_call": round(us, 2), "algorithmic_flops": flops,
         "tflops": round(tflops, 1), "peak_tflops": PEAK_TFLOPS,
         "frac": round(tflops / PEAK_TFLOPS, 4),
         "kv_gbps": round(kv / us / 1e3, 1),

@@ -414,7 +414,7 @@ def make_prefill(name: str, seed: int, dtype: str, num_q_heads: int, num_kv_head
                            ctx.astype(np.int32), starts, k_new, v_new, slots)
 
 
-PREFILL_WORKLOADS = ("llama13b_prefill", "gqa_chunked_prefill")
+PREFILL_WORKLOADS = ("llama13b_prefill", "gqa_chunked_prefill", "gqa_single_chunk_32k")
 
 
 def make_prefill_workload(name: str, poison: bool = True) -> PrefillWorkload:
@@ -425,7 +425,10 @@ def make_prefill_workload(name: str, poison: bool = True) -> PrefillWorkload:
       d 128, bs 16, bf16 -- the whole prompt is the chunk;
     * gqa_chunked_prefill: 16 sequences, 64 query heads over 8 KV heads, d 128,
       bs 16, bf16, a 512-token chunk on top of an earlier context of
-      lognormal(median 2048, sigma ln 2) tokens clipped to [256, 8192].
+      lognormal(median 2048, sigma ln 2) tokens clipped to [256, 8192];
+    * gqa_single_chunk_32k: one sequence, 64 query heads over 8 KV heads, d 128,
+      bs 16, bf16, a 64-token chunk on top of 32,704 earlier tokens (a long
+      conversation's next turn: few query rows, many keys).
     """
     if name == "llama13b_prefill":
         rng = np.random.default_rng(3110)
@@ -437,4 +440,6 @@ def make_prefill_workload(name: str, poison: bool = True) -> PrefillWorkload:
         prior = prior.astype(np.int64)
         return make_prefill(name, 3111, BF16, 64, 8, 128, 16, prior + 512,
                             np.full(16, 512), poison, rng)
+    if name == "gqa_single_chunk_32k":
+        return make_prefill(name, 3112, BF16, 64, 8, 128, 16, [32768], [64], poison)
     raise KeyError(f"unknown prefill workload {name!r}; choose from {PREFILL_WORKLOADS}")

@@ -185,3 +185,39 @@ def test_read_probe_rejects_bad_arguments_before_any_hip_call(lib):
     assert st(base=FAKE + 8) == 1                       # not 16-byte aligned
     assert st(n=(1 << 20) // 4096 + 1) == 1              # more tiles than the buffer holds
     assert st(n=0, checksum=None, base=None) == 0        # nothing to do
+
+
+def test_prefill_split_rejects_bad_arguments_before_any_hip_call(lib):
+    def st(splits, ws=None, ws_bytes=0, **kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tab=FAKE, mb=4, lens=FAKE, qs=FAKE, b=2, mq=8,
+                 t=10, hq=8, hkv=2, d=128, bs=16, nb=10, scale=0.1, dtype=1)
+        a.update(kw)
+        return lib.pa_prefill_split(a["out"], a["q"], a["k"], a["v"], a["tab"], a["mb"],
+                                    a["lens"], a["qs"], a["b"], a["mq"], a["t"], a["hq"],
+                                    a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"],
+                                    splits, ws, ws_bytes, None)
+    need = 3 * 10 * 8 * (128 + 4) * 4
+    assert st(-1) == 1
+    assert st(17) == 1
+    assert st(3, dtype=0) == 2
+    assert st(3) == 3                                     # no workspace
+    assert st(3, FAKE, need - 1) == 3                     # too small
+    assert st(3, FAKE + 8, need) == 3                     # not 16-byte aligned
+    assert st(3, b=0) == 0                                # nothing to do
+
+
+def test_prefill_split_plan(lib):
+    splits, nbytes = ctypes.c_int(-7), ctypes.c_size_t(7)
+
+    def plan(s, b=2, mq=8, t=10, hq=8, hkv=2, d=128, bs=16, mb=4):
+        return lib.pa_prefill_split_plan(b, mq, t, hq, hkv, d, bs, mb, s, ctypes.byref(splits),
+                                         ctypes.byref(nbytes))
+    assert plan(3) == 0 and splits.value == 3 and nbytes.value == 3 * 10 * 8 * 132 * 4
+    assert plan(16) == 0 and splits.value == 16 and nbytes.value == 16 * 10 * 8 * 132 * 4
+    assert plan(1) == 0 and splits.value == 1 and nbytes.value == 0
+    assert plan(17) == 1
+    assert plan(-1) == 1
+    assert plan(3, hq=6, hkv=4) == 1
+    assert plan(3, mb=0) == 1
+    assert lib.pa_prefill_split_plan(2, 8, 10, 8, 2, 128, 16, 4, 3, None,
+                                     ctypes.byref(nbytes)) == 1

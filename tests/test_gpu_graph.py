@@ -96,3 +96,42 @@ def test_prefill_replays_in_a_graph():
         g.replay()
         torch.cuda.synchronize()
         assert same(out, ref), f"replay {r}: output differs"
+
+
+def test_split_prefill_replays_in_a_graph():
+    """The split form is two kernels (split attention, then the merge of the
+    partial rows through the workspace); both capture."""
+    import paged_kv_cache_310_amd as pa
+    say("graph split prefill")
+    w = wl.make_prefill("graphsplit", 65, wl.BF16, 16, 2, 128, 16, [3000, 1000, 40], [64, 8, 40])
+    k, v = to_dev(w.k_cache), to_dev(w.v_cache)
+    pa.pa_append_kv(k, v, to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping))
+    q, tab = to_dev(w.q), to_dev(w.block_tables)
+    lens, qs = to_dev(w.context_lens), to_dev(w.query_start)
+    _, nbytes = pa.pa_prefill_split_plan(w.num_seqs, w.max_query_len, w.num_query_tokens, 16, 2,
+                                         128, 16, w.block_tables.shape[1], 6)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+
+    def call():
+        pa.pa_prefill(q, k, v, tab, lens, qs, float(w.scale), max_query_len=w.max_query_len,
+                      out=out, num_splits=6, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(5):
+        out.fill_(0)
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same(out, ref), f"replay {r}: output differs"
