@@ -517,6 +517,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
 // m = -inf and add nothing; the first split always holds key 0, which every
 // row sees.  Four waves of two rows each per workgroup, four dims per lane.
 constexpr int kMergeRowsPerWg = 8;
+constexpr int kMaxSplits = 16;
 __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a,
                                                             const SplitArgs sp) {
   const int64_t rows = sp.num_query_tokens * a.num_q_heads;
@@ -525,19 +526,34 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a,
   const int d0 = (threadIdx.x % 32) * 4;
   const int64_t split_stride = rows * kPartRow;
   const float* base = sp.partials + row * kPartRow;
+  const int n = sp.num_splits;
+  // Every split's loads are issued before the first is used (the bound is
+  // a constant; splits past n are skipped by a uniform branch).
+  float2 ml[kMaxSplits];
+  float4 o[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < n) {
+      const float* p = base + s * split_stride;
+      ml[s] = *reinterpret_cast<const float2*>(p + kPD);
+      o[s] = *reinterpret_cast<const float4*>(p + d0);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < sp.num_splits; ++s) M = fmaxf(M, base[s * split_stride + kPD]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < n) M = fmaxf(M, ml[s].x);
   float S = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < sp.num_splits; ++s) {
-    const float* p = base + s * split_stride;
-    const float2 ml = *reinterpret_cast<const float2*>(p + kPD);
-    const float f = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
-    const float4 o = *reinterpret_cast<const float4*>(p + d0);
-    S = fmaf(ml.y, f, S);
-    O[0] = fmaf(o.x, f, O[0]);
-    O[1] = fmaf(o.y, f, O[1]);
-    O[2] = fmaf(o.z, f, O[2]);
-    O[3] = fmaf(o.w, f, O[3]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < n) {
+      const float f = ml[s].x == -INFINITY ? 0.f : fast_exp2(ml[s].x - M);
+      S = fmaf(ml[s].y, f, S);
+      O[0] = fmaf(o[s].x, f, O[0]);
+      O[1] = fmaf(o[s].y, f, O[1]);
+      O[2] = fmaf(o[s].z, f, O[2]);
+      O[3] = fmaf(o[s].w, f, O[3]);
+    }
   }
   const float inv = 1.f / S;
   *reinterpret_cast<uint2*>(static_cast<char*>(a.out) + (row * kPD + d0) * 2) =
@@ -558,7 +574,7 @@ hipError_t launch_prefill_split(const PrefillArgs& a, int block_size, int num_sp
   const int64_t blocks = (int64_t)a.tiles_per_seq * kNumXcd *
                          ((a.num_seqs * a.num_kv_heads + kNumXcd - 1) / kNumXcd) * num_splits;
   if (blocks <= 0) return hipSuccess;
-  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (blocks > INT32_MAX || num_splits < 1 || num_splits > kMaxSplits) return hipErrorInvalidValue;
   const SplitArgs sp{num_splits, partials, num_query_tokens};
   const dim3 grid((unsigned)blocks), wg(kThreads);
   if (num_splits == 1) {
