@@ -285,14 +285,22 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
 // One wave per (decode worker, group of kMergeHeads query heads of its
 // segment); each lane owns 4 dims of one head.  A worker that closes a split
 // segment (its MergeRecord is valid) folds the pieces of workers first..w in
-// worker order, 8 pieces per batch: the batch's accumulator rows and (max,
-// sum) pairs are all loaded before any is used, with a running max across
-// batches, so a segment of up to 8 pieces costs one memory latency after the
-// record.  The fold order is fixed, so results are deterministic.  Runs after
+// worker order, kBatch pieces per batch: the batch's accumulator rows and
+// (max, sum) pairs are all loaded before any is used, with a running max
+// across batches, so a segment of up to kBatch pieces costs one memory
+// latency after the record.  The fold order is fixed for a given worker
+// count, so results are deterministic.  Runs after
 // the decode launch in stream order: the partials are visible without any
 // in-kernel fence.
 constexpr int kMergeWaves = 4;   // waves per merge workgroup
-constexpr int kMergeBatch = 8;   // pieces loaded together
+// Pieces loaded together.  Batches of many segments have few pieces per
+// segment: 8 at a time keeps the merge's registers low.  When the workers
+// average kMergeWideFrom or more pieces per segment (few sequences and KV
+// heads, where the worker cap leaves up to 48 per segment), a 32-wide
+// instance folds them in two rounds instead of six.
+constexpr int kMergeBatch = 8;
+constexpr int kMergeBatchWide = 32;
+constexpr int kMergeWideFrom = 16;
 
 template <int D>
 constexpr int merge_heads_per_wave() { return 64 / (D / 4); }
@@ -313,7 +321,7 @@ __device__ __forceinline__ void store_out4<float>(void* dst, const float* o, flo
   *reinterpret_cast<float4*>(dst) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
 }
 
-template <typename T, int D>
+template <typename T, int D, int kBatch>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArgs a, int workers) {
   constexpr int LPH = D / 4;                       // lanes per head
   constexpr int HPW = merge_heads_per_wave<D>();   // heads per wave
@@ -336,11 +344,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   const int npieces = w - (int)first + 1;
   float M = -INFINITY, S = 0.f;
   float O[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < npieces; p0 += kMergeBatch) {
-    float4 ob[kMergeBatch];
-    float2 mb[kMergeBatch];
+  for (int p0 = 0; p0 < npieces; p0 += kBatch) {
+    float4 ob[kBatch];
+    float2 mb[kBatch];
 #pragma unroll
-    for (int b = 0; b < kMergeBatch; ++b) {
+    for (int b = 0; b < kBatch; ++b) {
       const int p = p0 + b;
       if (p < npieces) {
         const int64_t slot = ((first + p) * 2 + (p == 0 ? first_slot : 0)) * G + g;
@@ -354,14 +362,14 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
     }
     float Mb = M;
 #pragma unroll
-    for (int b = 0; b < kMergeBatch; ++b) Mb = fmaxf(Mb, mb[b].x);
+    for (int b = 0; b < kBatch; ++b) Mb = fmaxf(Mb, mb[b].x);
     const float Mu = Mb == -INFINITY ? 0.f : Mb;
     const float alpha = fast_exp2(M - Mu);
     S *= alpha;
 #pragma unroll
     for (int e = 0; e < 4; ++e) O[e] *= alpha;
 #pragma unroll
-    for (int b = 0; b < kMergeBatch; ++b) {
+    for (int b = 0; b < kBatch; ++b) {
       const float f = fast_exp2(mb[b].x - Mu);
       S = fmaf(mb[b].y, f, S);
       O[0] = fmaf(ob[b].x, f, O[0]);
@@ -392,8 +400,12 @@ template <typename T, int D>
 hipError_t launch_merge(const DecodeArgs& a, int workers, hipStream_t stream) {
   const int hpw = merge_heads_per_wave<D>();
   const int64_t waves = (int64_t)workers * ((a.heads_per_seg + hpw - 1) / hpw);
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((waves + kMergeWaves - 1) / kMergeWaves)),
-                     dim3(64 * kMergeWaves), 0, stream, a, workers);
+  const dim3 grid((unsigned)((waves + kMergeWaves - 1) / kMergeWaves)), wg(64 * kMergeWaves);
+  const int64_t segments = (int64_t)a.num_seqs * (a.num_q_heads / a.heads_per_seg);
+  if ((int64_t)workers >= kMergeWideFrom * segments)
+    hipLaunchKernelGGL((merge_kernel<T, D, kMergeBatchWide>), grid, wg, 0, stream, a, workers);
+  else
+    hipLaunchKernelGGL((merge_kernel<T, D, kMergeBatch>), grid, wg, 0, stream, a, workers);
   return hipGetLastError();
 }
 
