@@ -42,7 +42,8 @@ KERNEL_SOURCES = {
     name: [os.path.join(ROOT, "paged_kv_cache_310_amd", "csrc", f)
            for f in (main, "decode_common.h", "pa_internal.h")]
     for name, main in (("decode_valu_kernel", "decode_kernel.hip"),
-                       ("decode_gqa_kernel", "gqa_kernel.hip"))
+                       ("decode_gqa_kernel", "gqa_kernel.hip"),
+                       ("prefill_kernel", "prefill_kernel.hip"))
 }
 
 
@@ -89,10 +90,11 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload: str, kernel: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary
-    of this workload, or None when absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_counters.md")
+def counter_traffic(workload: str, kernel: str, kind: str = "decode"):
+    """HBM bytes per attention launch (``kind`` decode or prefill) from the
+    committed rocprofv3 counter summary of this workload, or None when absent
+    or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -260,8 +262,10 @@ def run_prefill(args):
                    "heads": r["heads"], "head_dim": 128, "block_size": 16,
                    "context_splits": r["context_splits"]},
         "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": prefill_bench.PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": r["frac"], "traffic": None,
-                     "kernel": "prefill_kernel"},
+                     "unit": "TFLOP/s", "frac": r["frac"],
+                     "traffic": counter_traffic(r["workload"], "prefill_kernel", "prefill"),
+                     "kernel": "prefill_kernel",
+                     "kernel_source_sha256_16": kernel_source_hash("prefill_kernel")},
     }
     if args.cpu_seconds > 0:
         w = wl.make_prefill_workload(args.prefill_workload, poison=False)
