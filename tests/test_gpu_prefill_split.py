@@ -10,7 +10,9 @@ the same bf16 tolerance as pa_prefill (max-abs 2e-2, row max-rel 1e-2):
 * a zero and a negative scale;
 * the automatic choice on single long sequences with short chunks (the case
   splitting is for), on sampled rows;
-* repeat calls give identical bytes, and a workspace serves a smaller call.
+* repeat calls give identical bytes, and a workspace serves a smaller call;
+* PA_CHECK=1 rejects broken index arrays, and split counts past 16 are
+  rejected.
 """
 
 import numpy as np
@@ -127,3 +129,38 @@ def test_auto_split_single_long_sequence(ctx, nq):
     rows = _sample(w, 6, 8, 751)
     err = assert_attention_close(got, oracle_rows(w, rows=rows), wl.BF16, rows=rows)
     say("max-abs %.3e row-rel %.3e" % err)
+
+
+def test_split_checks_contract_under_pa_check():
+    """PA_CHECK=1 validates the index arrays of pa_prefill_split as it does
+    pa_prefill's, before launching; out-of-range split counts are rejected."""
+    import os
+    import subprocess
+    import sys
+    code = r"""
+import torch
+import paged_kv_cache_310_amd as pa
+from paged_kv_cache_310_amd._binding import PAError
+d = 'cuda:0'
+k = torch.zeros(8, 2, 16, 128, device=d, dtype=torch.bfloat16); v = torch.zeros_like(k)
+q = torch.zeros(5, 4, 128, device=d, dtype=torch.bfloat16)
+tab = torch.tensor([[0, 1], [2, 3]], dtype=torch.int32, device=d)
+i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=d)
+def status(f):
+    try:
+        f(); torch.cuda.synchronize(); return 0
+    except PAError as e:
+        return e.status
+S = dict(num_splits=3)
+print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 3]), i32([0, 2, 5]), 0.1, **S)))
+print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 2]), i32([0, 2, 5]), 0.1, **S)))
+print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 3]), i32([1, 2, 5]), 0.1, **S)))
+print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([40, 3]), i32([0, 2, 5]), 0.1, **S)))
+print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 3]), i32([0, 2, 5]), 0.1, num_splits=17)))
+print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 3]), i32([0, 2, 5]), 0.1, num_splits=0)))
+"""
+    env = dict(os.environ, PA_CHECK="1")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                         timeout=120, cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.split() == ["0", "5", "5", "5", "1", "0"], res.stdout
