@@ -217,17 +217,21 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
  * it was taken relative to, and its weight sum.  A second kernel then folds
  * the partial rows by the standard log-sum-exp rescaling.  Same arguments,
  * layouts and contract as pa_prefill, plus:
- *   num_splits      0 = automatic: 1 while the batch's row tiles (128 query
- *                   rows of one KV head each) fill the device's workgroup
- *                   slots (3 per compute unit) twice over.  Else the S in
- *                   2..Smax with the smallest ceil(tiles * S / CUs) / S (an
- *                   even share of workgroups per compute unit), the largest
- *                   S among equals; Smax = floor(2 * slots / tiles), at
- *                   least 2, at most 16 and at most one split per 16 key
- *                   steps of 32 keys of the longest context the tables
- *                   hold.  1 = no split (then exactly pa_prefill); 2..16 =
- *                   that many.  Beyond 16: PA_ERR_INVALID.  Splits change
- *                   only the fp32 summation order.
+ *   num_splits      0 = automatic, with tiles = the batch's row tiles (128
+ *                   query rows of one KV head each) and slots = 3 workgroups
+ *                   per compute unit:
+ *                     - 1 while tiles >= 2 * slots;
+ *                     - floor(slots / tiles), at most 32, while 16 * tiles
+ *                       <= slots (one full round of workgroups);
+ *                     - else the S in 2..Smax with the smallest
+ *                       ceil(tiles * S / CUs) / S (an even share per compute
+ *                       unit), the largest S among equals; Smax =
+ *                       floor(2 * slots / tiles), at least 2, at most 16;
+ *                   and never more than one split per 8 key steps of 32
+ *                   keys of the longest context the tables hold.
+ *                   1 = no split (then exactly pa_prefill); 2..32 = that
+ *                   many; beyond 32: PA_ERR_INVALID.  Splits change only the
+ *                   fp32 summation order.
  *   workspace       device memory of workspace_bytes, 16-byte aligned, at
  *                   least what pa_prefill_split_plan gives (with S splits:
  *                   S * num_query_tokens * num_q_heads * (head_dim + 4) *
@@ -246,7 +250,7 @@ int pa_prefill_split(void* out, const void* q, const void* k_cache, const void* 
 /* The split count pa_prefill_split uses for these sizes and num_splits
  * (0 = automatic, which reads the current device's compute-unit count) in
  * *splits, and the workspace it needs in *bytes.  PA_ERR_INVALID for sizes
- * pa_prefill would reject as invalid, or num_splits outside 0..16. */
+ * pa_prefill would reject as invalid, or num_splits outside 0..32. */
 int pa_prefill_split_plan(int num_seqs, int max_query_len, int64_t num_query_tokens,
                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                           int max_blocks_per_seq, int num_splits, int* splits, size_t* bytes);

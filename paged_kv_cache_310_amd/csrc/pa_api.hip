@@ -423,17 +423,20 @@ hipError_t launch_prefill_split(const PrefillArgs& a, int block_size, int num_sp
 
 namespace {
 
-constexpr int kPrefillMaxSplits = 16;
+constexpr int kPrefillMaxSplits = 32;
 constexpr int kPrefillWgsPerCu = 3;        // resident prefill workgroups per CU
-constexpr int kPrefillMinStepsPerSplit = 16;
+constexpr int kPrefillMinStepsPerSplit = 8;
+constexpr int kPrefillBalancedMaxSplits = 16;   // cap of the balanced choice
 
 // Splits pa_prefill_split picks for num_splits = 0.  None while the row tiles
-// alone fill the device's workgroup slots (3 per compute unit) twice.
-// Otherwise S in [2, Smax], Smax = floor(2 slots / tiles) (at least 2, at most
-// 16, and at most one split per 16 key steps of the longest context the
-// tables allow), with the smallest per-CU share ceil(tiles S / CUs) / S of one
-// tile's work -- splits that leave some CUs a workgroup more than others lose
-// -- and among equal shares the most splits (more resident workgroups).
+// alone fill the device's workgroup slots (3 per compute unit) twice.  When
+// even 16 splits would not fill one round of slots, as many as fill it (at
+// most 32).  Otherwise S in [2, Smax], Smax = floor(2 slots / tiles) (at
+// least 2, at most 16), with the smallest per-CU share ceil(tiles S / CUs) / S
+// of one tile's work -- splits that leave some CUs a workgroup more than
+// others lose -- and among equal shares the most splits (more resident
+// workgroups).  Either way at most one split per 8 key steps of the longest
+// context the tables allow.
 int prefill_auto_splits(int num_seqs, int max_query_len, int group, int num_kv_heads,
                         int max_blocks_per_seq, int block_size, int* splits) {
   int cus = 0;
@@ -444,12 +447,15 @@ int prefill_auto_splits(int num_seqs, int max_query_len, int group, int num_kv_h
   const int64_t wgs = tiles * num_seqs * num_kv_heads;
   const int64_t slots = (int64_t)cus * kPrefillWgsPerCu;
   const int64_t max_steps = ((int64_t)max_blocks_per_seq * block_size + 31) / 32;
+  const int64_t by_steps = max_steps / kPrefillMinStepsPerSplit;
   int64_t best = 1;
-  if (wgs > 0 && wgs < 2 * slots) {
+  if (wgs > 0 && wgs * kPrefillBalancedMaxSplits <= slots) {
+    best = slots / wgs;
+    best = best < kPrefillMaxSplits ? best : kPrefillMaxSplits;
+  } else if (wgs > 0 && wgs < 2 * slots) {
     int64_t smax = 2 * slots / wgs;
     smax = smax > 2 ? smax : 2;
-    smax = smax < kPrefillMaxSplits ? smax : kPrefillMaxSplits;
-    const int64_t by_steps = max_steps / kPrefillMinStepsPerSplit;
+    smax = smax < kPrefillBalancedMaxSplits ? smax : kPrefillBalancedMaxSplits;
     smax = smax < by_steps ? smax : by_steps;
     int64_t best_load = 0;
     for (int64_t n = 2; n <= smax; ++n) {
@@ -461,7 +467,8 @@ int prefill_auto_splits(int num_seqs, int max_query_len, int group, int num_kv_h
       }
     }
   }
-  *splits = (int)best;
+  best = best < by_steps ? best : by_steps;
+  *splits = (int)(best > 1 ? best : 1);
   return PA_OK;
 }
 

@@ -517,7 +517,10 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
 // m = -inf and add nothing; the first split always holds key 0, which every
 // row sees.  Four waves of two rows each per workgroup, four dims per lane.
 constexpr int kMergeRowsPerWg = 8;
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = 32;
+// kCap: split slots one lane holds in registers (16 or 32; the 32-slot
+// instance needs about twice the registers, so it serves only counts past 16).
+template <int kCap>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a,
                                                             const SplitArgs sp) {
   const int64_t rows = sp.num_query_tokens * a.num_q_heads;
@@ -528,11 +531,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a,
   const float* base = sp.partials + row * kPartRow;
   const int n = sp.num_splits;
   // Every split's loads are issued before the first is used (the bound is
-  // a constant; splits past n are skipped by a uniform branch).
-  float2 ml[kMaxSplits];
-  float4 o[kMaxSplits];
+  // the constant kCap; splits past n are skipped by a uniform branch).
+  float2 ml[kCap];
+  float4 o[kCap];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < kCap; ++s) {
     if (s < n) {
       const float* p = base + s * split_stride;
       ml[s] = *reinterpret_cast<const float2*>(p + kPD);
@@ -541,11 +544,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a,
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s)
+  for (int s = 0; s < kCap; ++s)
     if (s < n) M = fmaxf(M, ml[s].x);
   float S = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < kCap; ++s) {
     if (s < n) {
       const float f = ml[s].x == -INFINITY ? 0.f : fast_exp2(ml[s].x - M);
       S = fmaf(ml[s].y, f, S);
@@ -593,7 +596,10 @@ hipError_t launch_prefill_split(const PrefillArgs& a, int block_size, int num_sp
   const int64_t rows = num_query_tokens * a.num_q_heads;
   const int64_t wgs = (rows + kMergeRowsPerWg - 1) / kMergeRowsPerWg;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a, sp);
+  if (num_splits <= 16)
+    hipLaunchKernelGGL(prefill_merge_kernel<16>, dim3((unsigned)wgs), dim3(256), 0, stream, a, sp);
+  else
+    hipLaunchKernelGGL(prefill_merge_kernel<32>, dim3((unsigned)wgs), dim3(256), 0, stream, a, sp);
   return hipGetLastError();
 }
 

@@ -198,7 +198,7 @@ def test_prefill_split_rejects_bad_arguments_before_any_hip_call(lib):
                                     splits, ws, ws_bytes, None)
     need = 3 * 10 * 8 * (128 + 4) * 4
     assert st(-1) == 1
-    assert st(17) == 1
+    assert st(33) == 1
     assert st(3, dtype=0) == 2
     assert st(3) == 3                                     # no workspace
     assert st(3, FAKE, need - 1) == 3                     # too small
@@ -215,7 +215,8 @@ def test_prefill_split_plan(lib):
     assert plan(3) == 0 and splits.value == 3 and nbytes.value == 3 * 10 * 8 * 132 * 4
     assert plan(16) == 0 and splits.value == 16 and nbytes.value == 16 * 10 * 8 * 132 * 4
     assert plan(1) == 0 and splits.value == 1 and nbytes.value == 0
-    assert plan(17) == 1
+    assert plan(32) == 0 and splits.value == 32 and nbytes.value == 32 * 10 * 8 * 132 * 4
+    assert plan(33) == 1
     assert plan(-1) == 1
     assert plan(3, hq=6, hkv=4) == 1
     assert plan(3, mb=0) == 1

@@ -11,7 +11,7 @@ the same bf16 tolerance as pa_prefill (max-abs 2e-2, row max-rel 1e-2):
 * the automatic choice on single long sequences with short chunks (the case
   splitting is for), on sampled rows;
 * repeat calls give identical bytes, and a workspace serves a smaller call;
-* PA_CHECK=1 rejects broken index arrays, and split counts past 16 are
+* PA_CHECK=1 rejects broken index arrays, and split counts past 32 are
   rejected.
 """
 
@@ -61,7 +61,7 @@ RAGGED = [(1, 1), (17, 17), (100, 100), (200, 200), (2000, 40), (1000, 1), (513,
           (77, 0), (3000, 3)]
 
 
-@pytest.mark.parametrize("splits", [2, 3, 5, 16])
+@pytest.mark.parametrize("splits", [2, 3, 5, 16, 32])
 @pytest.mark.parametrize("hq,hkv,bs", [(8, 2, 16), (40, 40, 16), (16, 2, 32)])
 def test_forced_splits_ragged(hq, hkv, bs, splits):
     say("prefill split ragged", hq, hkv, bs, splits)
@@ -71,7 +71,7 @@ def test_forced_splits_ragged(hq, hkv, bs, splits):
     say("max-abs %.3e row-rel %.3e" % err)
 
 
-@pytest.mark.parametrize("splits", [3, 7, 16])
+@pytest.mark.parametrize("splits", [3, 7, 16, 32])
 @pytest.mark.parametrize("bs", [16, 32])
 def test_splits_cross_table_windows(bs, splits):
     """Contexts of 20k-40k keys span several 1024-entry table windows: split
@@ -133,7 +133,7 @@ def test_auto_split_single_long_sequence(ctx, nq):
 
 def test_split_checks_contract_under_pa_check():
     """PA_CHECK=1 validates the index arrays of pa_prefill_split as it does
-    pa_prefill's, before launching; out-of-range split counts are rejected."""
+    pa_prefill's, before launching; split counts past 32 are rejected."""
     import os
     import subprocess
     import sys
@@ -156,7 +156,7 @@ print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 3]), i32([0, 2, 5]), 0
 print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 2]), i32([0, 2, 5]), 0.1, **S)))
 print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 3]), i32([1, 2, 5]), 0.1, **S)))
 print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([40, 3]), i32([0, 2, 5]), 0.1, **S)))
-print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 3]), i32([0, 2, 5]), 0.1, num_splits=17)))
+print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 3]), i32([0, 2, 5]), 0.1, num_splits=33)))
 print(status(lambda: pa.pa_prefill(q, k, v, tab, i32([20, 3]), i32([0, 2, 5]), 0.1, num_splits=0)))
 """
     env = dict(os.environ, PA_CHECK="1")

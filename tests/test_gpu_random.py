@@ -86,7 +86,7 @@ def test_random_split_prefill(seed):
     whole = rng.random(b) < 0.25
     nq[whole] = np.minimum(ctx[whole], 400)
     ctx[whole] = nq[whole]
-    splits = int(rng.choice([0, 2, 3, 4, 6, 8, 11, 16]))
+    splits = int(rng.choice([0, 2, 3, 4, 6, 8, 11, 16, 24, 32]))
     say("split prefill case", seed, hkv, group, bs, ctx.tolist(), nq.tolist(), splits)
     w = wl.make_prefill("rsplit", seed, wl.BF16, hkv * group, hkv, 128, bs, ctx.tolist(),
                         nq.tolist())
