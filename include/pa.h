@@ -164,13 +164,15 @@ int pa_decode_default_workers(int* num_workers);
  *     slot of position context_lens[s]-1 of sequence s.
  *   workspace      see pa_decode_workspace_size (read/written)
  *   num_workers    0 = default: every worker resident at once (4 per
- *                  compute unit), but at most 48 per segment -- a (sequence,
+ *                  compute unit), but at most P per segment -- a (sequence,
  *                  KV head) pair on the matrix-core kernel, a (sequence,
  *                  query head) pair otherwise -- rounded up to a multiple of
  *                  8, so that small batches do not spend more time merging
- *                  split pieces than they gain; otherwise the exact number of
- *                  workers.  A tuning knob that changes only the fp32
- *                  summation order.
+ *                  split pieces than they gain.  P = max_blocks_per_seq *
+ *                  block_size / 128 (one piece per 8 16-token chunks of the
+ *                  table width), clamped to [16, 48].  Otherwise the exact
+ *                  number of workers.  A tuning knob that changes only the
+ *                  fp32 summation order.
  * Contract: 0 <= context_lens[s] <= max_blocks_per_seq * block_size; table
  * entries for the blocks a sequence uses lie in [0, num_blocks); entries past
  * them are never read. */

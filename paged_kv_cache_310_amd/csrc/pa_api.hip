@@ -124,23 +124,32 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
   return PA_OK;
 }
 
-// Default workers of one call: the variant's count, but at most
-// kMaxPiecesPerSegment workers per segment (a (sequence, head) pair of the
-// attention kernel's line), rounded up to a multiple of the XCD count.  A
-// segment split over more workers gains little kernel time and costs the
-// merge one more round of piece loads per 8 pieces: with one sequence and
-// 8 KV heads, 1,024 workers (128 pieces per segment) took 44 us per step
-// at a 4k context against 19 us at 384.
+// Default workers of one call: the variant's count, but at most P workers
+// per segment (a (sequence, head) pair of the attention kernel's line),
+// rounded up to a multiple of the XCD count.  A segment split over more
+// workers gains little kernel time and costs the merge more piece loads.
+// With one sequence and 8 KV heads, 1,024 workers (128 pieces per segment)
+// took 44 us per step at a 4k context, against 19 us at 384.  Short
+// contexts do best with fewer pieces (32 at 4k).  Up to 64 pieces helped
+// some longer shapes (one sequence, 32k) and cost others more merge time
+// than they gained (one sequence at 8k, two at 16k).  The host knows only
+// the table width, an upper bound of every context.  So P = one piece per 8
+// 16-token chunks of that width, clamped to [16, 48].
+constexpr int64_t kChunksPerPiece = 8;
+constexpr int64_t kMinPiecesPerSegment = 16;
 constexpr int64_t kMaxPiecesPerSegment = 48;
-int default_workers_for_call(int dtype, int head_dim, int block_size, int num_seqs,
-                             int num_q_heads, int num_kv_heads, int* out) {
+int default_workers_for_call(int dtype, int head_dim, int block_size, int max_blocks_per_seq,
+                             int num_seqs, int num_q_heads, int num_kv_heads, int* out) {
   const int group = num_q_heads / num_kv_heads;
   int workers = 0;
   const int st = default_workers_for_variant(dtype, head_dim, block_size, group, &workers);
   if (st != PA_OK) return st;
   const int64_t segments =
       (int64_t)num_seqs * (pa::gqa_supported(dtype, head_dim, group) ? num_kv_heads : num_q_heads);
-  int64_t cap = kMaxPiecesPerSegment * segments;
+  int64_t pieces = (int64_t)max_blocks_per_seq * block_size / 16 / kChunksPerPiece;
+  pieces = pieces < kMinPiecesPerSegment ? kMinPiecesPerSegment : pieces;
+  pieces = pieces > kMaxPiecesPerSegment ? kMaxPiecesPerSegment : pieces;
+  int64_t cap = pieces * segments;
   cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;
   *out = cap < workers ? (int)(cap > 0 ? cap : 1) : workers;
   return PA_OK;
@@ -353,8 +362,8 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
 
   int workers = num_workers;
   if (workers == 0) {
-    const int st = default_workers_for_call(dtype, head_dim, block_size, num_seqs, num_q_heads,
-                                            num_kv_heads, &workers);
+    const int st = default_workers_for_call(dtype, head_dim, block_size, max_blocks_per_seq,
+                                            num_seqs, num_q_heads, num_kv_heads, &workers);
     if (st != PA_OK) return st;
   }
   const int group = num_q_heads / num_kv_heads;
