@@ -130,14 +130,18 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
 // workers gains little kernel time and costs the merge more piece loads.
 // With one sequence and 8 KV heads, 1,024 workers (128 pieces per segment)
 // took 44 us per step at a 4k context, against 19 us at 384.  Short
-// contexts do best with fewer pieces (32 at 4k).  Up to 64 pieces helped
-// some longer shapes (one sequence, 32k) and cost others more merge time
-// than they gained (one sequence at 8k, two at 16k).  The host knows only
-// the table width, an upper bound of every context.  So P = one piece per 8
-// 16-token chunks of that width, clamped to [16, 48].
+// contexts do best with fewer pieces (32 at 4k).  The host knows only the
+// table width, an upper bound of every context, so P = one piece per 8
+// 16-token chunks of that width, clamped to [16, 48].  Tables of 2,048
+// chunks (32k tokens) or more take 64 pieces while that stays within half
+// the resident workers: one sequence at 32k-64k then gains 5-14% of its
+// step.  At 8k-16k, or with the device already full (two sequences at 32k),
+// the extra pieces cost more merge time than they save.
 constexpr int64_t kChunksPerPiece = 8;
 constexpr int64_t kMinPiecesPerSegment = 16;
 constexpr int64_t kMaxPiecesPerSegment = 48;
+constexpr int64_t kLongTableChunks = 2048;
+constexpr int64_t kLongTablePieces = 64;
 int default_workers_for_call(int dtype, int head_dim, int block_size, int max_blocks_per_seq,
                              int num_seqs, int num_q_heads, int num_kv_heads, int* out) {
   const int group = num_q_heads / num_kv_heads;
@@ -146,9 +150,12 @@ int default_workers_for_call(int dtype, int head_dim, int block_size, int max_bl
   if (st != PA_OK) return st;
   const int64_t segments =
       (int64_t)num_seqs * (pa::gqa_supported(dtype, head_dim, group) ? num_kv_heads : num_q_heads);
-  int64_t pieces = (int64_t)max_blocks_per_seq * block_size / 16 / kChunksPerPiece;
+  const int64_t chunks = (int64_t)max_blocks_per_seq * block_size / 16;
+  int64_t pieces = chunks / kChunksPerPiece;
   pieces = pieces < kMinPiecesPerSegment ? kMinPiecesPerSegment : pieces;
   pieces = pieces > kMaxPiecesPerSegment ? kMaxPiecesPerSegment : pieces;
+  if (chunks >= kLongTableChunks && kLongTablePieces * segments * 2 <= workers)
+    pieces = kLongTablePieces;
   int64_t cap = pieces * segments;
   cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;
   *out = cap < workers ? (int)(cap > 0 ? cap : 1) : workers;
