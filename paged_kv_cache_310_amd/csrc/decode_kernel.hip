@@ -293,13 +293,12 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
 // the decode launch in stream order: the partials are visible without any
 // in-kernel fence.
 constexpr int kMergeWaves = 4;   // waves per merge workgroup
-// Pieces loaded together.  Batches of many segments have few pieces per
-// segment: 8 at a time keeps the merge's registers low.  When the workers
-// average kMergeWideFrom or more pieces per segment (few sequences and KV
-// heads, where the worker cap leaves up to 48 per segment), a 32-wide
-// instance folds them in two rounds instead of six.
+// Pieces loaded together: 8 keeps the merge's registers low for batches of
+// many segments, which have few pieces each.  When the workers average
+// kMergeWideFrom or more pieces per segment (few sequences and KV heads,
+// where the worker cap leaves up to 64 per segment), merge_wide_kernel folds
+// each segment with a whole workgroup instead.
 constexpr int kMergeBatch = 8;
-constexpr int kMergeBatchWide = 32;
 constexpr int kMergeWideFrom = 16;
 
 template <int D>
@@ -385,6 +384,103 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   store_out4<T>(out_row + d0 * sizeof(T), O, 1.f / S);
 }
 
+// The merge for segments of many pieces (few sequences and heads, where the
+// worker cap allows up to 64 pieces per segment): one 4-wave workgroup per
+// (closing worker, head group).  Wave i folds a quarter of the segment's
+// pieces, all its loads in flight together (kWideBatch at a time), and the
+// four partial (max, sum, acc) results are combined through LDS.  The fold
+// order is fixed for a given worker count, so results are deterministic.
+constexpr int kWideBatch = 16;
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_wide_kernel(const DecodeArgs a,
+                                                                      int workers) {
+  constexpr int LPH = D / 4;                       // lanes per head
+  constexpr int HPW = merge_heads_per_wave<D>();   // heads per wave
+  __shared__ float4 s_acc[kMergeWaves][64];
+  __shared__ float2 s_ms[kMergeWaves][64];
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int hps = a.heads_per_seg;
+  const int wpr = (hps + HPW - 1) / HPW;           // head groups per record
+  const int id = (int)blockIdx.x;
+  const int w = id / wpr;
+  if (w >= workers) return;                        // whole workgroup
+  typedef __attribute__((address_space(4))) const MergeRecord const_record;
+  const const_record* r = (const const_record*)a.records + w;   // scalar loads
+  if (!r->valid) return;                           // whole workgroup
+  const int64_t first = r->first;
+  const int first_slot = r->first_slot;
+  const int g = (id - w * wpr) * HPW + lane / LPH;
+  const bool active = g < hps;
+  const int d0 = (lane % LPH) * 4;
+  const int G = a.group;
+  constexpr int REC = D + kPartialExtra;
+  const int npieces = w - (int)first + 1;
+  const int share = (npieces + kMergeWaves - 1) / kMergeWaves;
+  const int p_lo = min(npieces, wave * share);
+  const int p_hi = min(npieces, p_lo + share);
+  float M = -INFINITY, S = 0.f;
+  float O[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = p_lo; p0 < p_hi; p0 += kWideBatch) {
+    float4 ob[kWideBatch];
+    float2 mb[kWideBatch];
+#pragma unroll
+    for (int b = 0; b < kWideBatch; ++b) {
+      const int p = p0 + b;
+      if (active && p < p_hi) {
+        const int64_t slot = ((first + p) * 2 + (p == 0 ? first_slot : 0)) * G + g;
+        const float* rec = a.partials + slot * REC;
+        mb[b] = *reinterpret_cast<const float2*>(rec + D);
+        ob[b] = *reinterpret_cast<const float4*>(rec + d0);
+      } else {
+        mb[b] = make_float2(-INFINITY, 0.f);
+        ob[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int b = 0; b < kWideBatch; ++b) Mb = fmaxf(Mb, mb[b].x);
+    const float Mu = Mb == -INFINITY ? 0.f : Mb;
+    const float alpha = fast_exp2(M - Mu);
+    S *= alpha;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) O[e] *= alpha;
+#pragma unroll
+    for (int b = 0; b < kWideBatch; ++b) {
+      const float f = fast_exp2(mb[b].x - Mu);
+      S = fmaf(mb[b].y, f, S);
+      O[0] = fmaf(ob[b].x, f, O[0]);
+      O[1] = fmaf(ob[b].y, f, O[1]);
+      O[2] = fmaf(ob[b].z, f, O[2]);
+      O[3] = fmaf(ob[b].w, f, O[3]);
+    }
+    M = Mb;
+  }
+  s_acc[wave][lane] = make_float4(O[0], O[1], O[2], O[3]);
+  s_ms[wave][lane] = make_float2(M, S);
+  __syncthreads();
+  if (wave != 0 || !active) return;
+  float Mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMergeWaves; ++i) Mx = fmaxf(Mx, s_ms[i][lane].x);
+  float St = 0.f, Ot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kMergeWaves; ++i) {
+    const float2 ms = s_ms[i][lane];
+    const float4 o = s_acc[i][lane];
+    const float f = ms.x == -INFINITY ? 0.f : fast_exp2(ms.x - Mx);
+    St = fmaf(ms.y, f, St);
+    Ot[0] = fmaf(o.x, f, Ot[0]);
+    Ot[1] = fmaf(o.y, f, Ot[1]);
+    Ot[2] = fmaf(o.z, f, Ot[2]);
+    Ot[3] = fmaf(o.w, f, Ot[3]);
+  }
+  const int head = r->head * hps + g;
+  char* out_row =
+      static_cast<char*>(a.out) + ((size_t)r->seq * a.num_q_heads + head) * (D * sizeof(T));
+  store_out4<T>(out_row + d0 * sizeof(T), Ot, 1.f / St);
+}
+
 template <typename T, int D, int BS>
 hipError_t launch_valu(const DecodeArgs* a, int workers, hipStream_t stream, int* resident) {
   if (resident != nullptr) {
@@ -402,9 +498,11 @@ hipError_t launch_merge(const DecodeArgs& a, int workers, hipStream_t stream) {
   const int64_t waves = (int64_t)workers * ((a.heads_per_seg + hpw - 1) / hpw);
   const dim3 grid((unsigned)((waves + kMergeWaves - 1) / kMergeWaves)), wg(64 * kMergeWaves);
   const int64_t segments = (int64_t)a.num_seqs * (a.num_q_heads / a.heads_per_seg);
-  if ((int64_t)workers >= kMergeWideFrom * segments)
-    hipLaunchKernelGGL((merge_kernel<T, D, kMergeBatchWide>), grid, wg, 0, stream, a, workers);
-  else
+  if ((int64_t)workers >= kMergeWideFrom * segments) {
+    const int64_t groups = (int64_t)workers * ((a.heads_per_seg + hpw - 1) / hpw);
+    hipLaunchKernelGGL((merge_wide_kernel<T, D>), dim3((unsigned)groups), wg, 0, stream, a,
+                       workers);
+  } else
     hipLaunchKernelGGL((merge_kernel<T, D, kMergeBatch>), grid, wg, 0, stream, a, workers);
   return hipGetLastError();
 }
