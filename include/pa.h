@@ -171,7 +171,7 @@ int pa_decode_default_workers(int* num_workers);
  *                  split pieces than they gain.  P = max_blocks_per_seq *
  *                  block_size / 128 (one piece per 8 16-token chunks of the
  *                  table width), clamped to [16, 48]; 64 for tables of
- *                  2,048+ chunks (32k tokens) when 64 per segment stays
+ *                  1,024+ chunks (16k tokens) when 64 per segment stays
  *                  within half the resident workers.  Otherwise the exact
  *                  number of workers.  A tuning knob that changes only the
  *                  fp32 summation order.

@@ -132,15 +132,15 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
 // took 44 us per step at a 4k context, against 19 us at 384.  Short
 // contexts do best with fewer pieces (32 at 4k).  The host knows only the
 // table width, an upper bound of every context, so P = one piece per 8
-// 16-token chunks of that width, clamped to [16, 48].  Tables of 2,048
-// chunks (32k tokens) or more take 64 pieces while that stays within half
-// the resident workers: one sequence at 32k-64k then gains 5-14% of its
-// step.  At 8k-16k, or with the device already full (two sequences at 32k),
-// the extra pieces cost more merge time than they save.
+// 16-token chunks of that width, clamped to [16, 48].  Tables of 1,024
+// chunks (16k tokens) or more take 64 pieces while that stays within half
+// the resident workers: one sequence at 16k-64k then gains 5-14% of its
+// step.  At 8k, or with the device already full (two sequences at 16k or
+// 32k), the extra pieces cost more merge time than they save.
 constexpr int64_t kChunksPerPiece = 8;
 constexpr int64_t kMinPiecesPerSegment = 16;
 constexpr int64_t kMaxPiecesPerSegment = 48;
-constexpr int64_t kLongTableChunks = 2048;
+constexpr int64_t kLongTableChunks = 1024;
 constexpr int64_t kLongTablePieces = 64;
 int default_workers_for_call(int dtype, int head_dim, int block_size, int max_blocks_per_seq,
                              int num_seqs, int num_q_heads, int num_kv_heads, int* out) {
