@@ -77,6 +77,22 @@ def test_worker_counts(workers, group):
     assert_attention_close(out_f64(out), ref, wl.BF16)
 
 
+@pytest.mark.parametrize("dtype,d,hq,hkv", [(wl.FP32, 64, 4, 4), (wl.FP32, 128, 4, 4),
+                                             (wl.BF16, 64, 4, 4), (wl.BF16, 128, 16, 2)])
+@pytest.mark.parametrize("per_segment", [15, 16, 64])
+def test_merge_of_many_pieces(dtype, d, hq, hkv, per_segment):
+    """One long and one short sequence with many workers per segment: from 16
+    per segment on, segments are merged by a workgroup each (every wave folds a
+    quarter of the pieces); 15 stays on the one-wave merge."""
+    say("many pieces", dtype, d, hq, hkv, per_segment)
+    w = small(dtype, d, 16, hq, hkv, lens=[3000, 40], seed=13)
+    segments = 2 * (hkv if hq != hkv and dtype == wl.BF16 and d == 128 else hq)
+    ref = oracle_decode(w, *oracle_pools(w))
+    dw = DeviceWorkload(w)
+    out = dw.step(fused=True, num_workers=per_segment * segments)
+    assert_attention_close(out_f64(out), ref, dtype)
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = small(wl.BF16, 128, 16, 8, 8, seed=12)
     dw = DeviceWorkload(w)
