@@ -9,8 +9,8 @@ lognormal lengths with median 4096 clipped to [1024, 16384], bf16).
 
 Prints ONE JSON line: achieved HBM GB/s on the KV bytes the step reads
 (``value``), sequence-steps per second, the decode kernel's roofline entry
-(HIP-event timing, on the stream it runs on, of the attention launch of every
-tenth timed step) and the CPU oracle's throughput on a bounded sample of the
+(HIP-event timing, on the stream it runs on, of the attention launches of at
+least ten timed steps) and the CPU oracle's throughput on a bounded sample of the
 same workload.
 """
 
@@ -33,18 +33,24 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: achieved HBM GB/s (KV read) & % of peak; seq-steps/sec"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, vendor specification
-EVENT_EVERY = 10               # timed steps per step whose attention kernel is event-timed
-# Sources the decode kernels are built from; counter figures taken on other
-# versions of them are not reported.
-# Sources that define each attention kernel: a counter summary stays valid
-# while these are unchanged.
+EVENT_SAMPLES = 10             # attention launches event-timed per run (at least)
+# Sources that define each attention kernel and what runs with it in a step
+# (the merge kernels live in decode_kernel.hip): a counter summary stays
+# valid while these are unchanged.
+_CSRC = os.path.join(ROOT, "paged_kv_cache_310_amd", "csrc")
 KERNEL_SOURCES = {
-    name: [os.path.join(ROOT, "paged_kv_cache_310_amd", "csrc", f)
-           for f in (main, "decode_common.h", "pa_internal.h")]
-    for name, main in (("decode_valu_kernel", "decode_kernel.hip"),
-                       ("decode_gqa_kernel", "gqa_kernel.hip"),
-                       ("prefill_kernel", "prefill_kernel.hip"))
+    name: [os.path.join(_CSRC, f) for f in files + ("decode_common.h", "pa_internal.h")]
+    for name, files in (("decode_valu_kernel", ("decode_kernel.hip",)),
+                        ("decode_gqa_kernel", ("gqa_kernel.hip", "decode_kernel.hip")),
+                        ("prefill_kernel", ("prefill_kernel.hip",)))
 }
+
+
+def event_every(steps: int) -> int:
+    """Timed steps per step whose attention kernel is event-timed: every
+    step up to EVENT_SAMPLES steps, then spaced so that at least
+    EVENT_SAMPLES launches are timed."""
+    return max(1, steps // EVENT_SAMPLES)
 
 
 def attention_kernel_name(w) -> str:
@@ -338,12 +344,16 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # The attention kernel of every EVENT_EVERY-th timed step is bracketed by
-    # HIP events; recording them costs ~15 us of queue time per step, so doing
-    # it on every step would time the probe as much as the path.
-    sampled = list(range(0, args.steps, EVENT_EVERY))
+    # The attention kernel of every event_every(steps)-th timed step is
+    # bracketed by HIP events (at least EVENT_SAMPLES launches); recording
+    # them costs ~15 us of queue time per step, so doing it on every step of a
+    # long run would time the probe as much as the path.
+    sampled = list(range(0, args.steps, event_every(args.steps)))
     events = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for i in sampled}
+    for pair in events.values():      # torch creates an event on its first record:
+        for e in pair:                # do that here, outside the timed region
+            e.record()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):

@@ -10,8 +10,9 @@ data movement works on raw bit patterns, so it is exact.
 Sources (the three web pages about "Efficient Memory Management for Large
 Language Model Serving with PagedAttention"; cited by page and section):
 
-* [P1] phantomic12.github.io catalogue note, method paragraph ("Borrow
-  virtual memory paging ...").
+* [P1] phantomic12.github.io catalogue note, method paragraph: the KV cache
+  is cut into fixed-size blocks, and each request keeps a block table that
+  the attention kernels read through.
 * [P3] zeroshotmind.com essay, sections "Paging the cache", "Block tables:
   logical order, physical scatter", "Sharing a prefix without copying it".
 

@@ -255,16 +255,29 @@ def pa_read_probe(base, tile_ids=None, tile_bytes: int = 4096, nontemporal: bool
     return checksum
 
 
-def decode_workspace(device, nbytes: int) -> torch.Tensor:
-    """A workspace of at least ``nbytes`` for ``device``, reused by later
-    calls on the same device in stream order."""
+def decode_workspace(device, nbytes: int, stream=None) -> torch.Tensor:
+    """A workspace of at least ``nbytes`` for calls on ``stream`` (default:
+    the device's current stream), reused by later calls on that same stream.
+
+    A workspace must never serve two calls at once (include/pa.h), so each
+    stream has its own: calls on one stream are ordered, calls on two streams
+    are not.  The buffer is allocated while ``stream`` is current, so when a
+    larger one replaces it, torch's caching allocator hands the old memory
+    out again only in that stream's order, after the calls that used it."""
     device = torch.device(device)
-    key = (device.type, device.index)
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (device.type, device.index, int(s.cuda_stream))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def _check_workspace(workspace: torch.Tensor, ref: torch.Tensor) -> None:
+    _need(workspace.is_cuda and workspace.is_contiguous() and workspace.device == ref.device,
+          "workspace must be a contiguous device tensor on q's device")
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
@@ -279,7 +292,8 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
           and block_tables.shape[0] == b and block_tables.is_contiguous()
           and block_tables.device == q.device, "block_tables must be int32 [num_seqs, max_blocks]")
     _need(context_lens.dtype == torch.int32 and context_lens.shape == (b,)
-          and context_lens.device == q.device, "context_lens must be int32 [num_seqs]")
+          and context_lens.is_contiguous() and context_lens.device == q.device,
+          "context_lens must be a contiguous int32 [num_seqs] tensor")
     fused = [x is not None for x in (k_new, v_new, slot_mapping)]
     _need(all(fused) or not any(fused), "k_new, v_new and slot_mapping go together")
     if all(fused):
@@ -287,14 +301,16 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
             _need(x.shape == (b, hkv, d) and x.dtype == q.dtype and x.is_contiguous()
                   and x.device == q.device, "k_new/v_new must be [num_seqs, num_kv_heads, head_dim]")
         _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (b,)
-              and slot_mapping.device == q.device, "slot_mapping must be int64 [num_seqs]")
+              and slot_mapping.is_contiguous() and slot_mapping.device == q.device,
+              "slot_mapping must be a contiguous int64 [num_seqs] tensor")
     if out is None:
         out = torch.empty_like(q)
     _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
           and out.device == q.device, "out must match q")
     need = pa_decode_workspace_size(b, hq, hkv, d, num_workers)
     if workspace is None:
-        workspace = decode_workspace(q.device, need)
+        workspace = decode_workspace(q.device, need, stream)
+    _check_workspace(workspace, q)
     _call("pa_decode", _load().pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), b, hq, hkv, d, bs, nb, float(scale),
@@ -357,8 +373,7 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, sca
         _, nbytes = pa_prefill_split_plan(b, int(max_query_len), t, hq, hkv, d, bs,
                                           block_tables.shape[1], int(num_splits))
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    _need(workspace.is_cuda and workspace.is_contiguous() and workspace.device == q.device,
-          "workspace must be a contiguous device tensor on q's device")
+    _check_workspace(workspace, q)
     _call("pa_prefill_split", _load().pa_prefill_split(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), _ptr(query_start), b, int(max_query_len), t,

@@ -301,6 +301,54 @@ print(status(lambda: pa.pa_read_probe(k, torch.tensor([0, 15], dtype=torch.int32
     assert res.stdout.split() == ["5", "5", "5", "5", "5", "0", "0", "5", "0"], res.stdout
 
 
+def test_binding_rejects_strided_index_arrays_before_any_launch():
+    """Strided views of the lengths, the slots or the workspace would make the
+    kernels read raw memory past the data: the binding refuses them."""
+    import paged_kv_cache_310_amd as pa
+    w = small(wl.BF16, 128, 16, 8, 8, lens=[5, 17, 40, 64])
+    d = DeviceWorkload(w)
+    lens2 = torch.stack([d.lens, d.lens], 1).reshape(-1)[::2]
+    slots2 = torch.stack([d.slots, d.slots], 1).reshape(-1)[::2]
+    assert not lens2.is_contiguous() and not slots2.is_contiguous()
+    with pytest.raises(ValueError):
+        pa.pa_decode(d.q, d.k, d.v, d.tables, lens2, float(w.scale))
+    with pytest.raises(ValueError):
+        pa.pa_decode(d.q, d.k, d.v, d.tables, d.lens, float(w.scale), k_new=d.k_new,
+                     v_new=d.v_new, slot_mapping=slots2)
+    ws = torch.zeros(2 * pa.pa_decode_workspace_size(4, 8, 8, 128), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        pa.pa_decode(d.q, d.k, d.v, d.tables, d.lens, float(w.scale), workspace=ws[::2])
+    with pytest.raises(ValueError):
+        pa.pa_decode(d.q, d.k, d.v, d.tables, d.lens, float(w.scale), workspace=ws.cpu())
+
+
+def test_streams_get_their_own_default_workspace():
+    """Calls on two streams without an explicit workspace must not share one
+    (they may run at once): outputs on each stream equal the single-stream
+    result, for two shapes back to back."""
+    import paged_kv_cache_310_amd as pa
+    from paged_kv_cache_310_amd import _binding
+    a = DeviceWorkload(small(wl.BF16, 128, 16, 8, 8, lens=[300, 1000, 17, 513], append=False))
+    b = DeviceWorkload(small(wl.BF16, 128, 16, 16, 2, lens=[2000, 64, 700], append=False))
+    ref_a = pa.pa_decode(a.q, a.k, a.v, a.tables, a.lens, float(a.w.scale))
+    ref_b = pa.pa_decode(b.q, b.k, b.v, b.tables, b.lens, float(b.w.scale))
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            oa = pa.pa_decode(a.q, a.k, a.v, a.tables, a.lens, float(a.w.scale))
+        with torch.cuda.stream(s2):
+            ob = pa.pa_decode(b.q, b.k, b.v, b.tables, b.lens, float(b.w.scale))
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        assert torch.equal(oa.view(torch.int16), ref_a.view(torch.int16))
+        assert torch.equal(ob.view(torch.int16), ref_b.view(torch.int16))
+    keys = {k for k in _binding._workspaces if k[2] in (s1.cuda_stream, s2.cuda_stream)}
+    assert len(keys) == 2
+
+
 # ---------------------------------------------------------- full-size workloads
 @pytest.fixture(scope="module")
 def cache():
@@ -356,8 +404,12 @@ def test_workload_shared_prefix_steady(cache):
     _check_full(_full(cache, "shared_prefix_steady"))
 
 
-def test_workload_shared_prefix_fork(cache):
-    _check_full(_full(cache, "shared_prefix_fork"), fused=False)
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
+def test_workload_shared_prefix_fork(cache, fused):
+    """The fork step as the benchmark times it (the 112 copy-on-write copies,
+    then decode with the append fused), and with a separate append: whole
+    pools bit-exact, outputs of every sequence."""
+    _check_full(_full(cache, "shared_prefix_fork"), fused=fused)
 
 
 @pytest.mark.parametrize("name", ["gqa_pareto_bs16", "gqa_pareto_bs32"])
