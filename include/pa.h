@@ -261,10 +261,12 @@ int pa_prefill_split_plan(int num_seqs, int max_query_len, int64_t num_query_tok
 
 /* Measurement hook.  `before` and `after` are hipEvent_t handles (created by
  * the caller).  While set, every pa_decode call made from this host thread
- * records `before` on its stream immediately before launching the attention
- * kernel and `after` immediately after it -- before the small kernel that
- * merges split context pieces -- so the attention kernel alone can be timed.
- * Pass NULL, NULL to stop.  Returns PA_ERR_INVALID if exactly one is NULL. */
+ * launches its attention kernel with `before` and `after` as the launch's
+ * start and stop events (hipExtLaunchKernel): they take the kernel's own
+ * start and end times, without the small kernel that merges split context
+ * pieces and without marker packets between the kernels, so the attention
+ * kernel alone can be timed at no cost to the step.  Pass NULL, NULL to
+ * stop.  Returns PA_ERR_INVALID if exactly one is NULL. */
 int pa_set_decode_events(void* before, void* after);
 
 /* Read-bandwidth probe (measurement only; not a step of the paged path).

@@ -280,10 +280,10 @@ def _check_workspace(workspace: torch.Tensor, ref: torch.Tensor) -> None:
           "workspace must be a contiguous device tensor on q's device")
 
 
-def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
-              k_new=None, v_new=None, slot_mapping=None, workspace=None, num_workers: int = 0,
-              stream=None) -> torch.Tensor:
-    """Decode-step paged attention; returns ``out`` [num_seqs, num_q_heads, head_dim]."""
+def _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, out, k_new, v_new,
+                       slot_mapping):
+    """Checks pa_decode's tensors; returns the pool shape and ``out`` (made
+    when not given)."""
     nb, hkv, bs, d = _check_cache(k_cache, v_cache)
     _need(q.dim() == 3 and q.shape[2] == d and q.dtype == k_cache.dtype and q.is_contiguous()
           and q.device == k_cache.device, "q must be [num_seqs, num_q_heads, head_dim] like the pools")
@@ -307,6 +307,16 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
         out = torch.empty_like(q)
     _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
           and out.device == q.device, "out must match q")
+    return (nb, hkv, bs, d), out
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
+              k_new=None, v_new=None, slot_mapping=None, workspace=None, num_workers: int = 0,
+              stream=None) -> torch.Tensor:
+    """Decode-step paged attention; returns ``out`` [num_seqs, num_q_heads, head_dim]."""
+    (nb, hkv, bs, d), out = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                               out, k_new, v_new, slot_mapping)
+    b, hq, _ = q.shape
     need = pa_decode_workspace_size(b, hq, hkv, d, num_workers)
     if workspace is None:
         workspace = decode_workspace(q.device, need, stream)

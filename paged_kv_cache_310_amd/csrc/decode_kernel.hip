@@ -259,7 +259,7 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
                     f32x4_bits(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]));
       }
       if (lane == 0) queue_put(q, f, D * 4, f32x4_bits(m, l, 0.f, 0.f));
-      queue_job(q, f, a.partials + ((int64_t)w * 2 + mt.partial_slot()) * a.group * REC, REC * 4,
+      queue_job(q, f, a.partials + ((int64_t)w * 2 + mt.partial_slot()) * a.piece_rows * REC, REC * 4,
                 lane);
     }
   };
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
   const int g = (id - w * wpr) * HPW + lane / LPH;
   if (g >= hps) return;   // no cross-lane work follows
   const int d0 = (lane % LPH) * 4;
-  const int G = a.group;
+  const int R = a.piece_rows;
   constexpr int REC = D + kPartialExtra;   // acc[D], max, sum, pad
   const int npieces = w - (int)first + 1;
   float M = -INFINITY, S = 0.f;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArg
     for (int b = 0; b < kBatch; ++b) {
       const int p = p0 + b;
       if (p < npieces) {
-        const int64_t slot = ((first + p) * 2 + (p == 0 ? first_slot : 0)) * G + g;
+        const int64_t slot = ((first + p) * 2 + (p == 0 ? first_slot : 0)) * R + g;
         const float* rec = a.partials + slot * REC;
         mb[b] = *reinterpret_cast<const float2*>(rec + D);
         ob[b] = *reinterpret_cast<const float4*>(rec + d0);
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_wide_kernel(const Deco
   const int g = (id - w * wpr) * HPW + lane / LPH;
   const bool active = g < hps;
   const int d0 = (lane % LPH) * 4;
-  const int G = a.group;
+  const int R = a.piece_rows;
   constexpr int REC = D + kPartialExtra;
   const int npieces = w - (int)first + 1;
   const int share = (npieces + kMergeWaves - 1) / kMergeWaves;
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_wide_kernel(const Deco
     for (int b = 0; b < kWideBatch; ++b) {
       const int p = p0 + b;
       if (active && p < p_hi) {
-        const int64_t slot = ((first + p) * 2 + (p == 0 ? first_slot : 0)) * G + g;
+        const int64_t slot = ((first + p) * 2 + (p == 0 ? first_slot : 0)) * R + g;
         const float* rec = a.partials + slot * REC;
         mb[b] = *reinterpret_cast<const float2*>(rec + D);
         ob[b] = *reinterpret_cast<const float4*>(rec + d0);
@@ -482,13 +482,15 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_wide_kernel(const Deco
 }
 
 template <typename T, int D, int BS>
-hipError_t launch_valu(const DecodeArgs* a, int workers, hipStream_t stream, int* resident) {
+hipError_t launch_valu(const DecodeArgs* a, int workers, hipStream_t stream, int* resident,
+                       hipEvent_t start, hipEvent_t stop) {
   if (resident != nullptr) {
     // Resident one-wave workgroups per CU for this variant (occupancy query).
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
         resident, reinterpret_cast<const void*>(&decode_valu_kernel<T, D, BS>), 64, 0);
   }
-  hipLaunchKernelGGL((decode_valu_kernel<T, D, BS>), dim3(workers), dim3(64), 0, stream, *a);
+  hipExtLaunchKernelGGL((decode_valu_kernel<T, D, BS>), dim3(workers), dim3(64), 0, stream, start,
+                        stop, 0, *a);
   return hipGetLastError();
 }
 
@@ -509,10 +511,11 @@ hipError_t launch_merge(const DecodeArgs& a, int workers, hipStream_t stream) {
 
 // The vector-ALU attention kernel for one variant, or its occupancy.
 hipError_t dispatch_valu(const DecodeArgs* a, int dtype, int head_dim, int block_size,
-                         int workers, hipStream_t stream, int* resident) {
+                         int workers, hipStream_t stream, int* resident,
+                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
 #define PA_DISPATCH(T, DT, HD, BSZ)                                          \
   if (dtype == DT && head_dim == HD && block_size == BSZ)                    \
-    return launch_valu<T, HD, BSZ>(a, workers, stream, resident);
+    return launch_valu<T, HD, BSZ>(a, workers, stream, resident, start, stop);
   PA_DISPATCH(uint16_t, kBf16, 128, 16)
   PA_DISPATCH(uint16_t, kBf16, 128, 32)
   PA_DISPATCH(uint16_t, kBf16, 64, 16)
@@ -541,13 +544,15 @@ hipError_t launch_decode(const DecodeArgs& args, int dtype, int head_dim, int bl
   DecodeArgs a = args;
   const bool mfma = gqa_supported(dtype, head_dim, a.group);
   a.heads_per_seg = mfma ? a.group : 1;
+  a.piece_rows = a.heads_per_seg;
   a.seg_cost = mfma ? kSegCostMfma : kSegCostValu;
-  hipError_t e = hipSuccess;
-  if (before != nullptr && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
-  e = mfma ? launch_gqa_attention(a, block_size, workers, stream, nullptr)
-           : dispatch_valu(&a, dtype, head_dim, block_size, workers, stream, nullptr);
+  // The events, when set, take the attention kernel's own start and end
+  // times from its dispatch (no marker packets between the kernels).
+  const hipError_t e =
+      mfma ? launch_gqa_attention(a, block_size, workers, stream, nullptr, before, after)
+           : dispatch_valu(&a, dtype, head_dim, block_size, workers, stream, nullptr, before,
+                           after);
   if (e != hipSuccess) return e;
-  if (after != nullptr && (e = hipEventRecord(after, stream)) != hipSuccess) return e;
   if (workers == 1) return hipSuccess;   // one worker never splits a segment
   return dispatch_merge(a, dtype, head_dim, workers, stream);
 }

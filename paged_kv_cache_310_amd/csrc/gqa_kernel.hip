@@ -303,7 +303,8 @@ void decode_gqa_kernel(const DecodeArgs a) {
         }
         if (g4 == 0) queue_put(q, f, (n * REC + kD) * 4, f32x4_bits(m, l, 0.f, 0.f));
       }
-      queue_job(q, f, a.partials + ((int64_t)w * 2 + mt.partial_slot()) * G * REC, bytes, lane);
+      queue_job(q, f, a.partials + ((int64_t)w * 2 + mt.partial_slot()) * a.piece_rows * REC,
+                bytes, lane);
     }
   };
 
@@ -331,19 +332,22 @@ bool gqa_supported(int dtype, int head_dim, int group) {
 }
 
 hipError_t launch_gqa_attention(const DecodeArgs& a, int block_size, int workers,
-                                hipStream_t stream, int* resident) {
+                                hipStream_t stream, int* resident, hipEvent_t start,
+                                hipEvent_t stop) {
   if (block_size == 16) {
     if (resident != nullptr)
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
           resident, reinterpret_cast<const void*>(&decode_gqa_kernel<16>), 64, 0);
-    hipLaunchKernelGGL((decode_gqa_kernel<16>), dim3(workers), dim3(64), 0, stream, a);
+    hipExtLaunchKernelGGL((decode_gqa_kernel<16>), dim3(workers), dim3(64), 0, stream, start,
+                          stop, 0, a);
     return hipGetLastError();
   }
   if (block_size == 32) {
     if (resident != nullptr)
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(
           resident, reinterpret_cast<const void*>(&decode_gqa_kernel<32>), 64, 0);
-    hipLaunchKernelGGL((decode_gqa_kernel<32>), dim3(workers), dim3(64), 0, stream, a);
+    hipExtLaunchKernelGGL((decode_gqa_kernel<32>), dim3(workers), dim3(64), 0, stream, start,
+                          stop, 0, a);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

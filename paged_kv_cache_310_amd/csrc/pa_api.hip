@@ -345,13 +345,43 @@ int pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, in
   return PA_OK;
 }
 
-int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
-              const int32_t* block_tables, int max_blocks_per_seq,
-              const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
-              int head_dim, int block_size, int64_t num_blocks, float scale,
-              const void* k_new, const void* v_new, const int64_t* slot_mapping,
-              void* workspace, size_t workspace_bytes, int num_workers,
-              int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode's checks and launch.
+int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
+                const int32_t* block_tables, int max_blocks_per_seq,
+                const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                int head_dim, int block_size, int64_t num_blocks, float scale,
+                const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                void* workspace, size_t workspace_bytes, int num_workers,
+                int dtype, void* stream);
+
+}  // namespace
+
+extern "C" int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                         int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                         float scale, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, void* workspace, size_t workspace_bytes,
+                         int num_workers, int dtype, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     k_new, v_new, slot_mapping, workspace, workspace_bytes, num_workers,
+                     dtype, stream);
+}
+
+namespace {
+
+int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
+                const int32_t* block_tables, int max_blocks_per_seq,
+                const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                int head_dim, int block_size, int64_t num_blocks, float scale,
+                const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                void* workspace, size_t workspace_bytes, int num_workers,
+                int dtype, void* stream) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_workers < 0 ||
       !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks) ||
       num_q_heads % num_kv_heads != 0 || !(scale == scale))
@@ -374,7 +404,8 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
     if (st != PA_OK) return st;
   }
   const int group = num_q_heads / num_kv_heads;
-  const size_t need = pa::partials_bytes(workers, group, head_dim);
+  const size_t need =
+      pa::partials_bytes(workers, pa::decode_piece_rows(dtype, head_dim, group), head_dim);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -428,7 +459,7 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
              : PA_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace
 
 namespace pa {
 // Prefill with the context split over num_splits workgroups per row tile

@@ -2,6 +2,7 @@
 // Not part of the public ABI (that is include/pa.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,13 +52,14 @@ struct DecodeArgs {
   const void* v_new;
   const int64_t* slot_mapping;
   MergeRecord* records;       // [workers]
-  float* partials;            // [workers][2][group][head_dim + 4]: acc, max, sum, pad
+  float* partials;            // [workers][2][piece_rows][head_dim + 4]: acc, max, sum, pad
   int64_t max_blocks_per_seq;
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
   int group;                  // num_q_heads / num_kv_heads
   int heads_per_seg;          // query heads one work segment covers (1, or group on MFMA)
+  int piece_rows;             // rows (query heads) per partial piece slot: heads_per_seg
   int seg_cost;               // work units a segment costs besides its chunks
   float scale_log2;           // scale * log2(e): scores live in the exp2 domain
 };
@@ -73,13 +75,13 @@ __host__ __device__ inline int partial_floats(int head_dim) { return head_dim + 
 inline size_t records_bytes(int workers) {
   return ((size_t)workers * sizeof(MergeRecord) + 255) & ~(size_t)255;
 }
-inline size_t partials_bytes(int workers, int group, int head_dim) {
+inline size_t partials_bytes(int workers, int rows, int head_dim) {
   return records_bytes(workers) +
-         (size_t)workers * 2 * (size_t)group * (size_t)partial_floats(head_dim) * sizeof(float);
+         (size_t)workers * 2 * (size_t)rows * (size_t)partial_floats(head_dim) * sizeof(float);
 }
 
-// Launches the attention kernel (recording `before`/`after`, when not null,
-// around it) and then the merge kernel.
+// Launches the attention kernel (with `before`/`after`, when not null, as its
+// start and stop events) and then the merge kernel.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,
                          int workers, hipStream_t stream, hipEvent_t before, hipEvent_t after);
 // Resident decode workers (one-wave workgroups) per CU for a variant.
@@ -89,8 +91,14 @@ hipError_t decode_resident_per_cu(int dtype, int head_dim, int block_size, int g
 // 2 <= group <= 16.  Launches the attention kernel only, or reports its
 // occupancy when resident != nullptr.
 bool gqa_supported(int dtype, int head_dim, int group);
+// Rows of one partial piece of pa_decode: the query heads of a segment (the
+// group on the matrix-core kernel, one head on the vector kernel).
+inline int decode_piece_rows(int dtype, int head_dim, int group) {
+  return gqa_supported(dtype, head_dim, group) ? group : 1;
+}
 hipError_t launch_gqa_attention(const DecodeArgs& a, int block_size, int workers,
-                                hipStream_t stream, int* resident);
+                                hipStream_t stream, int* resident, hipEvent_t start = nullptr,
+                                hipEvent_t stop = nullptr);
 // Multi-token (prefill) attention: what the kernel reads, by value.
 struct PrefillArgs {
   void* out;
