@@ -186,6 +186,34 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
               void* workspace, size_t workspace_bytes, int num_workers,
               int dtype, void* stream);
 
+/* pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture that must not call hipMalloc, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, semantics, contract and kernels as
+ * pa_decode, without the workspace: the merge records and partial results live
+ * in a static device array of PA_NOALLOC_SCRATCH_BYTES bytes that each GPU the
+ * library runs on holds from this entry point's first call on it until the
+ * process ends.  The call allocates and frees nothing.
+ *   Its need is what pa_decode needs for these sizes with bf16 head_dim 128
+ *   and 2..16 query heads per KV head (the matrix-core kernel):
+ *   num_workers * 2 * group * (head_dim + 4) * 4 bytes plus 48 bytes per
+ *   worker (rounded up to 256); otherwise num_workers * 2 * (head_dim + 4) * 4
+ *   bytes plus the same records.  The default worker count of every shape
+ *   fits on a 256-CU device (at most 1,024 workers: 17.4 MB for groups of
+ *   16); a need above PA_NOALLOC_SCRATCH_BYTES (an explicit num_workers) is
+ *   rejected with PA_ERR_WORKSPACE before any launch.
+ *   The array needs no initialisation: every call writes what it reads.
+ * All calls on one GPU share its one array, so two pa_decode_noalloc calls
+ * that can overlap on one GPU (different streams, or different host threads
+ * without ordering) race and give wrong results; calls ordered on one stream
+ * are safe.  PA_ERR_UNSUPPORTED for device ordinals of 64 and above. */
+#define PA_NOALLOC_SCRATCH_BYTES (24u << 20)
+int pa_decode_noalloc(void* out, const void* q, void* k_cache, void* v_cache,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                      float scale, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, int num_workers, int dtype, void* stream);
+
 /* Multi-token (prompt / chunked-prompt) paged attention.  Pages: catalogue
  * note, method paragraph (attention reads through the block table) and
  * "Block tables: logical order, physical scatter" (logical order = the

@@ -70,6 +70,9 @@ def _load():
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i64,
                                   ctypes.c_float, vp, vp, vp, vp, sz, i32, i32, vp]
         lib.pa_decode.restype = i32
+        lib.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                          i64, ctypes.c_float, vp, vp, vp, i32, i32, vp]
+        lib.pa_decode_noalloc.restype = i32
         lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i64, i32, i32, i32,
                                    i32, i64, ctypes.c_float, i32, vp]
         lib.pa_prefill.restype = i32
@@ -326,6 +329,23 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
         block_tables.shape[1], _ptr(context_lens), b, hq, hkv, d, bs, nb, float(scale),
         _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(workspace),
         workspace.numel() * workspace.element_size(), int(num_workers), _dtype_code(q),
+        _stream(q.device, stream)))
+    return out
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
+                      k_new=None, v_new=None, slot_mapping=None, num_workers: int = 0,
+                      stream=None) -> torch.Tensor:
+    """``pa_decode`` whose workspace is the library's static device scratch
+    array: the library call allocates nothing (``out`` is allocated here only
+    when not given).  Calls that can overlap on one GPU race (include/pa.h)."""
+    (nb, hkv, bs, d), out = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                               out, k_new, v_new, slot_mapping)
+    b, hq, _ = q.shape
+    _call("pa_decode_noalloc", _load().pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), b, hq, hkv, d, bs, nb, float(scale),
+        _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), int(num_workers), _dtype_code(q),
         _stream(q.device, stream)))
     return out
 

@@ -349,13 +349,15 @@ int pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, in
 
 namespace {
 
-// pa_decode's checks and launch.
+// pa_decode's checks and launch.  `workspace` is the caller's workspace, or
+// -- for pa_decode_noalloc -- null, with `scratch` the current device's static
+// scratch array: the need is then checked against its size.
 int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
                 const int32_t* block_tables, int max_blocks_per_seq,
                 const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                 int head_dim, int block_size, int64_t num_blocks, float scale,
                 const void* k_new, const void* v_new, const int64_t* slot_mapping,
-                void* workspace, size_t workspace_bytes, int num_workers,
+                void* workspace, size_t workspace_bytes, bool use_scratch, int num_workers,
                 int dtype, void* stream);
 
 }  // namespace
@@ -369,8 +371,53 @@ extern "C" int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
                          int num_workers, int dtype, void* stream) {
   return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
-                     k_new, v_new, slot_mapping, workspace, workspace_bytes, num_workers,
+                     k_new, v_new, slot_mapping, workspace, workspace_bytes, false, num_workers,
                      dtype, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode without any allocation: the workspace is a file-scope device array.
+// Each device that runs the library holds its own copy of `scratch` until the
+// process ends.  In host code its name is only a host-side stand-in: the
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is ever handed to kernels.
+static_assert(PA_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use).
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return PA_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_decode_noalloc(void* out, const void* q, void* k_cache, void* v_cache,
+                                 const int32_t* block_tables, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int64_t num_blocks, float scale, const void* k_new,
+                                 const void* v_new, const int64_t* slot_mapping, int num_workers,
+                                 int dtype, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     k_new, v_new, slot_mapping, nullptr, 0, true, num_workers, dtype, stream);
 }
 
 namespace {
@@ -380,7 +427,7 @@ int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
                 const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                 int head_dim, int block_size, int64_t num_blocks, float scale,
                 const void* k_new, const void* v_new, const int64_t* slot_mapping,
-                void* workspace, size_t workspace_bytes, int num_workers,
+                void* workspace, size_t workspace_bytes, bool use_scratch, int num_workers,
                 int dtype, void* stream) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_workers < 0 ||
       !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks) ||
@@ -406,6 +453,12 @@ int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
   const int group = num_q_heads / num_kv_heads;
   const size_t need =
       pa::partials_bytes(workers, pa::decode_piece_rows(dtype, head_dim, group), head_dim);
+  if (use_scratch) {
+    if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+    const int sc = scratch_for_current_device(&workspace);
+    if (sc != PA_OK) return sc;
+    workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
