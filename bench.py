@@ -41,7 +41,10 @@ _CSRC = os.path.join(ROOT, "paged_kv_cache_310_amd", "csrc")
 KERNEL_SOURCES = {
     name: [os.path.join(_CSRC, f) for f in files + ("decode_common.h", "pa_internal.h")]
     for name, files in (("decode_valu_kernel", ("decode_kernel.hip",)),
-                        ("decode_gqa_kernel", ("gqa_kernel.hip", "decode_kernel.hip")),
+                        ("decode_gqa_kernel", ("gqa_kernel.hip", "gqa_body.h", "merge_body.h",
+                                               "decode_kernel.hip")),
+                        ("decode_shared_kernel", ("shared_kernel.hip", "gqa_body.h",
+                                                  "merge_body.h")),
                         ("prefill_kernel", ("prefill_kernel.hip",)))
 }
 
@@ -53,11 +56,15 @@ def event_every(steps: int) -> int:
     return max(1, steps // EVENT_SAMPLES)
 
 
-def attention_kernel_name(w) -> str:
-    """The attention kernel pa_decode launches for this workload: the
-    matrix-core kernel for bf16 head_dim 128 with 2..16 query heads per KV
-    head, else the vector kernel."""
+def attention_kernel_name(w, shared: bool = False) -> str:
+    """The attention kernel the step launches for this workload: with the
+    groups (pa_decode_shared) the shared-prefix kernel for bf16 head_dim 128
+    and 1..16 query heads per KV head; pa_decode's matrix-core kernel for
+    bf16 head_dim 128 with 2..16 query heads per KV head; else the vector
+    kernel."""
     group = w.num_q_heads // w.num_kv_heads
+    if shared and w.dtype == "bf16" and w.head_dim == 128 and 1 <= group <= 16:
+        return "decode_shared_kernel"
     if w.dtype == "bf16" and w.head_dim == 128 and 2 <= group <= 16:
         return "decode_gqa_kernel"
     return "decode_valu_kernel"
@@ -74,6 +81,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama13b_long")
     p.add_argument("--workers", type=int, default=0, help="decode workers (0 = library default)")
+    p.add_argument("--plain", action="store_true",
+                   help="time pa_decode even when the workload has groups sharing a prefix "
+                        "(default for such workloads: pa_decode_shared)")
     p.add_argument("--cold-steps", type=int, default=20,
                    help="extra steps, each after a 512 MiB write that evicts the MALL")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -111,22 +121,35 @@ def counter_traffic(workload: str, kernel: str, kind: str = "decode"):
     return float(t.group(1))
 
 
-def decode_tile_order(w) -> np.ndarray:
+def decode_tile_order(w, shared: bool = False) -> np.ndarray:
     """Tile ids (16-token tiles of a pool, in address order) in the order the
     decode kernels walk them: KV head by KV head, each sequence's cached
-    tokens in logical order through its block table."""
+    tokens in logical order through its block table.  ``shared``: each
+    group's shared chunks once (through its first member's table), then every
+    sequence's remaining chunks."""
     cpb = w.block_size // 16
     per_head = []
+
+    def tiles(s, c):
+        blocks = w.block_tables[s, c // cpb].astype(np.int64)
+        return blocks * w.num_kv_heads * cpb + c % cpb
+
+    start = np.zeros(w.num_seqs, np.int64)
+    if shared:
+        lens = w.context_lens.astype(np.int64)
+        start = np.minimum(np.maximum(w.prefix_lens.astype(np.int64), 0), lens) // 16
+        for g in range(len(w.group_start) - 1):
+            lo, hi = int(w.group_start[g]), int(w.group_start[g + 1])
+            if hi > lo:
+                per_head.append(tiles(lo, np.arange(start[lo])))
     for s in range(w.num_seqs):
         n = -(-int(w.context_lens[s]) // 16)
-        c = np.arange(n)
-        blocks = w.block_tables[s, c // cpb].astype(np.int64)
-        per_head.append(blocks * w.num_kv_heads * cpb + c % cpb)
+        per_head.append(tiles(s, np.arange(start[s], n)))
     base = np.concatenate(per_head) if per_head else np.zeros(0, np.int64)
     return np.concatenate([base + h * cpb for h in range(w.num_kv_heads)]).astype(np.int32)
 
 
-def read_ceiling(pa, k, v, w, workers: int, reps: int = 5):
+def read_ceiling(pa, k, v, w, workers: int, reps: int = 5, shared: bool = False):
     """Bandwidth of the decode kernels' access pattern without their
     arithmetic, measured on the same pools in the same run with
     pa_read_probe (K plain, V non-temporal, as the attention kernels load
@@ -139,7 +162,7 @@ def read_ceiling(pa, k, v, w, workers: int, reps: int = 5):
         return None
     gen = torch.Generator(device="cpu").manual_seed(3199)
     ntiles = k.numel() * k.element_size() // tile
-    ids_dec = torch.from_numpy(decode_tile_order(w)).to(k.device)
+    ids_dec = torch.from_numpy(decode_tile_order(w, shared)).to(k.device)
     ids_k = torch.randperm(ntiles, generator=gen).to(torch.int32).to(k.device)
     ids_v = torch.randperm(ntiles, generator=gen).to(torch.int32).to(k.device)
 
@@ -324,19 +347,26 @@ def main():
     k_new, v_new, slots, pairs = to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping), \
         to_dev(w.block_mapping)
     out = torch.empty_like(q)
-    ws_bytes = pa.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                           args.workers)
+    shared = w.group_start is not None and not args.plain
+    size_fn = pa.pa_decode_shared_workspace_size if shared else pa.pa_decode_workspace_size
+    ws_bytes = size_fn(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, args.workers)
     workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    gstart, plens = (to_dev(w.group_start), to_dev(w.prefix_lens)) if shared else (None, None)
 
     def step(ev=None):
         if pairs is not None:
             pa.pa_copy_blocks(k, v, pairs)
         if ev is not None:
-            # the library records these right around the attention kernel
+            # the library passes these as the attention launch's own events
             pa.pa_set_decode_events(ev[0], ev[1])
-        pa.pa_decode(q, k, v, tables, lens, float(w.scale), out=out, k_new=k_new, v_new=v_new,
-                     slot_mapping=slots, workspace=workspace, num_workers=args.workers)
+        if shared:
+            pa.pa_decode_shared(q, k, v, tables, lens, float(w.scale), gstart, plens, out=out,
+                                k_new=k_new, v_new=v_new, slot_mapping=slots,
+                                workspace=workspace, num_workers=args.workers)
+        else:
+            pa.pa_decode(q, k, v, tables, lens, float(w.scale), out=out, k_new=k_new,
+                         v_new=v_new, slot_mapping=slots, workspace=workspace,
+                         num_workers=args.workers)
         if ev is not None:
             pa.pa_set_decode_events(None, None)
 
@@ -385,13 +415,17 @@ def main():
         cold_write_ms = float(np.median(cold_write))
         del sweep
 
-    probe = read_ceiling(pa, k, v, w, args.workers) if args.probe else None
+    probe = read_ceiling(pa, k, v, w, args.workers, shared=shared) if args.probe else None
 
-    kv = w.kv_bytes
+    # Bytes the step must read: every cached token's K and V rows for every
+    # KV head -- with the groups, each group's shared tokens once.
+    kv = w.kv_shared_read_bytes if shared else w.kv_bytes
     avg_kernel_s = float(kernel_ms.mean()) / 1e3
     achieved = kv / avg_kernel_s / 1e9
     value = kv / (ms_per_step / 1e3) / 1e9
-    traffic = counter_traffic(w.name, attention_kernel_name(w))
+    kernel = attention_kernel_name(w, shared)
+    traffic = counter_traffic(w.name + ("" if shared or w.group_start is None else "_plain"),
+                              kernel)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -409,10 +443,14 @@ def main():
             "workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
             "context_tokens": int(w.context_lens.sum()), "kv_bytes_per_step": kv,
+            "logical_kv_bytes_per_step": w.kv_bytes,
             "step": ("copy + " if pairs is not None else "")
-                    + ("fused append + decode" if slots is not None else "decode"),
+                    + ("fused append + " if slots is not None else "")
+                    + ("decode with shared prefixes read once per group" if shared else "decode"),
+            "groups": None if w.group_start is None else int(len(w.group_start) - 1),
             "workers": args.workers or "default",
         },
+        "logical_kv_gbps": round(w.kv_bytes / (ms_per_step / 1e3) / 1e9, 2),
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "seq_steps_per_s": round(w.num_seqs / (ms_per_step / 1e3), 1),
         "decode_kernel_ms": {"launches_timed": len(kernel_ms),
@@ -428,8 +466,8 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": attention_kernel_name(w),
-            "kernel_source_sha256_16": kernel_source_hash(attention_kernel_name(w)),
+            "kernel": kernel,
+            "kernel_source_sha256_16": kernel_source_hash(kernel),
         },
         "device": torch.cuda.get_device_name(dev),
         "host": platform.node(),

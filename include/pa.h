@@ -5,7 +5,9 @@
  *   pa_append_kv    write new tokens' keys/values into the slots a slot mapping names;
  *   pa_copy_blocks  copy whole blocks (the copy in copy-on-write);
  *   pa_decode       one decode step of attention for every sequence, reading each
- *                   sequence's keys/values through its block table.
+ *                   sequence's keys/values through its block table
+ *                   (pa_decode_shared: the same, reading tokens that groups of
+ *                   sequences share once per group);
  *   pa_prefill      attention of a multi-token query chunk per sequence (a prompt,
  *                   or a piece of one) with a causal mask, through the block table;
  * and, for a model whose layers each own a pool, layer-batched forms of the
@@ -185,6 +187,53 @@ int pa_decode(void* out, const void* q, void* k_cache, void* v_cache,
               const void* k_new, const void* v_new, const int64_t* slot_mapping,
               void* workspace, size_t workspace_bytes, int num_workers,
               int dtype, void* stream);
+
+/* Bytes of device workspace pa_decode_shared needs for these sizes and
+ * num_workers (0 = the library's default for the current device), whichever
+ * of its paths the call takes.  Writes *bytes.  It holds what pa_decode's
+ * workspace holds (partial slots of 16 rows per worker) plus, per sequence
+ * and KV head, two 16-byte locators and, per sequence and query head, two
+ * result rows of head_dim + 4 floats.  No initialisation needed; one
+ * workspace serves successive calls in stream order (never two at once). */
+int pa_decode_shared_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int num_workers, size_t* bytes);
+
+/* Decode-step paged attention for a batch whose sequences come in groups that
+ * share a prefix -- samples forked from one prompt, beams of one request.
+ * Page: zeroshotmind.com essay, "Sharing a prefix without copying it" (the
+ * sharers' block tables point at the same physical blocks, so one copy of the
+ * prefix serves all of them); "Block tables: logical order, physical scatter".
+ * Computes exactly what pa_decode computes with the same arguments (the same
+ * out, the same fused append, within the fp32 summation order), but reads
+ * the shared tokens once per group instead of once per member: each shared
+ * 16-token tile of a KV head is read once for all the group's query rows.
+ *   group_start   int32 [num_groups + 1], device: group g is the sequences
+ *                 group_start[g] <= s < group_start[g + 1] (consecutive)
+ *   num_groups    0 = no groups: plain pa_decode
+ *   prefix_lens   int32 [num_seqs], device: tokens at the start of sequence s
+ *                 that it shares with the rest of its group (0 = none)
+ *   Everything else as pa_decode; workspace per pa_decode_shared_workspace_size.
+ * Contract (checked under PA_CHECK=1): group_start[0] = 0, non-decreasing,
+ * group_start[num_groups] = num_seqs; 0 <= prefix_lens[s] <= context_lens[s],
+ * and < context_lens[s] when the fused append writes sequence s (the new
+ * token is never shared); prefix_lens equal within a group; the block-table
+ * entries of the first ceil(prefix_lens[s] / block_size) blocks of every
+ * member equal those of the group's first sequence.  The shared part of a
+ * sequence is its first floor(prefix_lens[s] / 16) * 16 tokens; the rest is
+ * read through its own table.
+ * Paths: bf16, head_dim 128 and 1..16 query heads per KV head run the shared
+ * kernels (one attention launch, whose workers split between the groups'
+ * shared tokens and the sequences' own tokens, and one merge); other shapes
+ * run pa_decode's kernels.  num_workers as pa_decode (the shared kernels use
+ * at least 2).  pa_set_decode_events times the attention launch. */
+int pa_decode_shared(void* out, const void* q, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* context_lens, int num_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                     float scale, const void* k_new, const void* v_new,
+                     const int64_t* slot_mapping, const int32_t* group_start, int num_groups,
+                     const int32_t* prefix_lens, void* workspace, size_t workspace_bytes,
+                     int num_workers, int dtype, void* stream);
 
 /* pa_decode for callers that cannot allocate device memory: code under HIP
  * graph capture that must not call hipMalloc, tight serving loops, harnesses

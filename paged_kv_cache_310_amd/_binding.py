@@ -73,6 +73,13 @@ def _load():
         lib.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                           i64, ctypes.c_float, vp, vp, vp, i32, i32, vp]
         lib.pa_decode_noalloc.restype = i32
+        lib.pa_decode_shared.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                         i64, ctypes.c_float, vp, vp, vp, vp, i32, vp, vp, sz,
+                                         i32, i32, vp]
+        lib.pa_decode_shared.restype = i32
+        lib.pa_decode_shared_workspace_size.argtypes = [i32, i32, i32, i32, i32,
+                                                        ctypes.POINTER(sz)]
+        lib.pa_decode_shared_workspace_size.restype = i32
         lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i64, i32, i32, i32,
                                    i32, i64, ctypes.c_float, i32, vp]
         lib.pa_prefill.restype = i32
@@ -330,6 +337,45 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
         _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(workspace),
         workspace.numel() * workspace.element_size(), int(num_workers), _dtype_code(q),
         _stream(q.device, stream)))
+    return out
+
+
+def pa_decode_shared_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                    head_dim: int, num_workers: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _call("pa_decode_shared_workspace_size", _load().pa_decode_shared_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers, ctypes.byref(out)))
+    return int(out.value)
+
+
+def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, scale, group_start,
+                     prefix_lens, out=None, k_new=None, v_new=None, slot_mapping=None,
+                     workspace=None, num_workers: int = 0, stream=None) -> torch.Tensor:
+    """Decode-step paged attention over groups of sequences that share a
+    prefix: the same result as ``pa_decode``, reading each group's shared
+    tokens once.  ``group_start`` int32 [num_groups + 1] (groups are runs of
+    consecutive sequences), ``prefix_lens`` int32 [num_seqs] (tokens each
+    sequence shares with its group)."""
+    (nb, hkv, bs, d), out = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                               out, k_new, v_new, slot_mapping)
+    b, hq, _ = q.shape
+    _need(group_start.dtype == torch.int32 and group_start.dim() == 1
+          and group_start.numel() >= 1 and group_start.is_contiguous()
+          and group_start.device == q.device,
+          "group_start must be a contiguous int32 [num_groups + 1] tensor on q's device")
+    _need(prefix_lens.dtype == torch.int32 and prefix_lens.shape == (b,)
+          and prefix_lens.is_contiguous() and prefix_lens.device == q.device,
+          "prefix_lens must be a contiguous int32 [num_seqs] tensor on q's device")
+    need = pa_decode_shared_workspace_size(b, hq, hkv, d, num_workers)
+    if workspace is None:
+        workspace = decode_workspace(q.device, need, stream)
+    _check_workspace(workspace, q)
+    _call("pa_decode_shared", _load().pa_decode_shared(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), b, hq, hkv, d, bs, nb, float(scale),
+        _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(group_start), group_start.numel() - 1,
+        _ptr(prefix_lens), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        int(num_workers), _dtype_code(q), _stream(q.device, stream)))
     return out
 
 

@@ -387,6 +387,8 @@ struct Cursor {
   int64_t seg_start;
   int64_t slot;
   int h, s, L, n, j;
+  int j0;   // the segment's first chunk on this line: 0, or on the tail line of a
+            // shared-prefix decode the first chunk after the sequence's shared prefix
 };
 
 __device__ __forceinline__ int64_t append_slot(const int64_t* slot_mapping, int s) {
@@ -403,6 +405,7 @@ __device__ __forceinline__ void cursor_start(Cursor& k, const SplitLds& C, const
   k.L = uniform(seq_len(C, lens, k.s));
   k.slot = append_slot(slots, k.s);
   k.n = chunks_of(k.L);
+  k.j0 = 0;
   k.j = (int)(ls.b0 - k.seg_start);
 }
 
@@ -422,6 +425,7 @@ __device__ __forceinline__ void cursor_next(Cursor& k, const int32_t* lens_ptr,
     k.slot = append_slot(slots, k.s);
   } while (k.L == 0);
   k.n = chunks_of(k.L);
+  k.j0 = 0;
   k.j = 0;
   k.seg_start = k.c;
 }
@@ -434,6 +438,7 @@ enum ChunkFlags : int {
   kLast = 2,     // last chunk of the segment in this worker's range
   kWhole = 4,    // the whole segment lies in this worker's range
   kSecond = 8,   // the segment begins inside the range: partial slot 1
+  kGrouped = 16, // tail line: the sequence's shared prefix is attended to elsewhere
 };
 
 struct ChunkMeta {
@@ -445,6 +450,7 @@ struct ChunkMeta {
   __device__ bool last() const { return flags & kLast; }
   __device__ bool whole() const { return flags & kWhole; }
   __device__ int partial_slot() const { return (flags & kSecond) ? 1 : 0; }
+  __device__ bool grouped() const { return flags & kGrouped; }
 };
 
 __device__ __forceinline__ ChunkMeta chunk_meta(const Cursor& k, int64_t b0, int64_t b1) {
@@ -452,15 +458,168 @@ __device__ __forceinline__ ChunkMeta chunk_meta(const Cursor& k, int64_t b0, int
   m.h = k.h;
   m.s = k.s;
   const bool seg_last = k.j == k.n - 1;
-  m.flags = ((k.c == b0 || k.j == 0) ? kFirst : 0) | ((k.c == b1 - 1 || seg_last) ? kLast : 0) |
-            ((k.seg_start >= b0 && k.seg_start + k.n <= b1) ? kWhole : 0) |
-            (k.seg_start > b0 ? kSecond : 0);
+  m.flags = ((k.c == b0 || k.j == k.j0) ? kFirst : 0) | ((k.c == b1 - 1 || seg_last) ? kLast : 0) |
+            ((k.seg_start >= b0 && k.seg_start + (k.n - k.j0) <= b1) ? kWhole : 0) |
+            (k.seg_start > b0 ? kSecond : 0) | (k.j0 > 0 ? kGrouped : 0);
   m.slot = seg_last ? k.slot : -1;
   // The appended token's pool slot is not written yet: it is attended to
   // from k_new/v_new instead.
   const int pool = k.L - (m.slot >= 0 ? 1 : 0) - k.j * kChunk;
   m.valid = pool < kChunk ? pool : kChunk;
   return m;
+}
+
+// ---------------------------------------------------------------------------
+// The tail line of a shared-prefix decode.  A sequence whose first P tokens
+// are shared with the other members of its group has its first
+// floor(P / 16) chunks attended to by the group's prefix pass; the tail line
+// holds only its remaining chunks.  Per sequence the line's chunk count is
+// chunks_of(L) - shared_chunks(L, P) (0: the sequence has no tail segment).
+
+// Chunks of a sequence of length L covered by a shared prefix of P tokens
+// (P clamped into [0, L]: an out-of-contract P never reads past the context).
+__device__ __forceinline__ int shared_chunks(int L, int P) {
+  P = P < 0 ? 0 : (P > L ? L : P);
+  return P / kChunk;
+}
+
+// Line chunks and units of the tail line (per head), caching each sequence's
+// line chunk count in C.len (the split's LDS cache, here holding counts).
+__device__ __forceinline__ void tail_line_totals(SplitLds& C, const int32_t* lens,
+                                                 const int32_t* prefix_lens, int num_seqs,
+                                                 int seg_cost, int lane, int64_t& wseq,
+                                                 int64_t& useq) {
+  wseq = 0;
+  useq = 0;
+  for (int base = 0; base < num_seqs; base += 256) {
+    int64_t n = 0, un = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sq = base + k * 64 + lane;
+      if (sq < num_seqs) {
+        const int L = lens[sq];
+        const int c = chunks_of(L) - shared_chunks(L, prefix_lens[sq]);
+        if (sq < kLenCache) ((lds_i32*)C.len)[sq] = c;
+        n += c;
+        un += c > 0 ? c + seg_cost : 0;
+      }
+    }
+    wseq += uniform(wave_sum(n));
+    useq += uniform(wave_sum(un));
+  }
+}
+
+__device__ __forceinline__ int tail_count(const SplitLds& C, const int32_t* lens,
+                                          const int32_t* prefix_lens, int s) {
+  if (s < kLenCache) return ((const lds_i32*)C.len)[s];
+  const int L = lens[s];
+  return chunks_of(L) - shared_chunks(L, prefix_lens[s]);
+}
+
+// locate_units over the tail line's per-sequence counts.
+__device__ void tail_locate_units(const SplitLds& C, const int32_t* lens,
+                                  const int32_t* prefix_lens, int num_seqs, int seg_cost,
+                                  int64_t r0, int64_t r1, int lane, UnitHit& h0, UnitHit& h1) {
+  h0.found = false;
+  h1.found = false;
+  int64_t acc_u = 0, acc_ne = 0;
+  for (int base = 0; base < num_seqs && !(h0.found && h1.found); base += 64) {
+    const int sq = base + lane;
+    const int n = sq < num_seqs ? tail_count(C, lens, prefix_lens, sq) : 0;
+    const int un = n > 0 ? n + seg_cost : 0;
+    const unsigned long long ne = __ballot(n > 0);
+    int64_t incl;
+    if (__ballot(un >= (1 << 24)) == 0) {
+      incl = wave_inclusive_scan32(un);
+    } else {
+      incl = wave_inclusive_scan((int64_t)un, lane);
+    }
+    const int64_t tot = uniform((int64_t)__shfl(incl, 63));
+    auto probe = [&](int64_t r, UnitHit& hit) {
+      if (hit.found || r >= acc_u + tot) return;
+      const unsigned long long above = __ballot(acc_u + incl > r);
+      const int first = __ffsll((long long)above) - 1;
+      hit.found = true;
+      hit.s = uniform(base + first);
+      hit.bu = uniform((int64_t)(acc_u + __shfl(incl - un, first)));
+      const int64_t ne_before = acc_ne + __popcll(ne & ((1ull << first) - 1));
+      hit.bc = hit.bu - (int64_t)seg_cost * ne_before;
+      hit.off = r - hit.bu;
+    };
+    probe(r0, h0);
+    probe(r1, h1);
+    acc_u += tot;
+    acc_ne += __popcll(ne);
+  }
+}
+
+// The split of the tail line for worker w of nworkers, given its totals per
+// head; false when w has no chunks.
+__device__ __forceinline__ bool tail_split(const SplitLds& C, const int32_t* lens,
+                                           const int32_t* prefix_lens, int num_seqs,
+                                           int num_heads, int seg_cost, int64_t wseq,
+                                           int64_t useq, int nworkers, int w, int lane,
+                                           LineSplit& ls) {
+  ls.wseq = wseq;
+  ls.useq = useq;
+  ls.W = wseq * num_heads;
+  ls.U = useq * num_heads;
+  if (ls.U == 0) return false;
+  ls.NW = ls.U < nworkers ? ls.U : nworkers;
+  if (w >= ls.NW) return false;
+  ls.u0 = (int64_t)w * ls.U / ls.NW;
+  ls.u1 = (int64_t)(w + 1) * ls.U / ls.NW;
+  const int hh0 = (int)(ls.u0 / ls.useq);
+  const int hh1 = ls.u1 < ls.U ? (int)(ls.u1 / ls.useq) : 0;
+  const int64_t r1 = ls.u1 < ls.U ? ls.u1 - (int64_t)hh1 * ls.useq : ls.U;
+  UnitHit x0, x1;
+  tail_locate_units(C, lens, prefix_lens, num_seqs, seg_cost, ls.u0 - (int64_t)hh0 * ls.useq, r1,
+                    lane, x0, x1);
+  ls.h = hh0;
+  ls.s = x0.s;
+  ls.seg_start = (int64_t)hh0 * ls.wseq + x0.bc;
+  ls.seg_unit = (int64_t)hh0 * ls.useq + x0.bu;
+  ls.b0 = ls.seg_start + (x0.off < seg_cost ? 0 : x0.off - seg_cost);
+  ls.b1 = ls.u1 < ls.U ? (int64_t)hh1 * ls.wseq + x1.bc + (x1.off < seg_cost ? 0 : x1.off - seg_cost)
+                       : ls.W;
+  return ls.b0 < ls.b1;
+}
+
+// Places a tail-line cursor on the first chunk of a worker's range.
+__device__ __forceinline__ void tail_cursor_start(Cursor& k, const int32_t* lens,
+                                                  const int32_t* prefix_lens,
+                                                  const int64_t* slots, const LineSplit& ls) {
+  k.c = ls.b0;
+  k.h = ls.h;
+  k.s = ls.s;
+  k.seg_start = ls.seg_start;
+  k.L = uniform(((const const_i32*)lens)[k.s]);
+  k.j0 = uniform(shared_chunks(k.L, ((const const_i32*)prefix_lens)[k.s]));
+  k.slot = append_slot(slots, k.s);
+  k.n = chunks_of(k.L);
+  k.j = k.j0 + (int)(ls.b0 - k.seg_start);
+}
+
+// Moves a tail-line cursor to the next chunk, skipping sequences without a tail.
+__device__ __forceinline__ void tail_cursor_next(Cursor& k, const int32_t* lens_ptr,
+                                                 const int32_t* prefix_ptr, const int64_t* slots,
+                                                 int num_seqs) {
+  const const_i32* lens = (const const_i32*)lens_ptr;   // scalar loads (lgkmcnt)
+  const const_i32* plen = (const const_i32*)prefix_ptr;
+  ++k.c;
+  if (++k.j < k.n) return;
+  do {
+    if (++k.s == num_seqs) {
+      k.s = 0;
+      ++k.h;
+    }
+    k.L = lens[k.s];
+    k.j0 = shared_chunks(k.L, plen[k.s]);
+    k.slot = append_slot(slots, k.s);
+  } while (chunks_of(k.L) - k.j0 == 0);
+  k.n = chunks_of(k.L);
+  k.j = k.j0;
+  k.seg_start = k.c;
 }
 
 // ---------------------------------------------------------------------------

@@ -40,7 +40,7 @@
 //  * Fused append: the worker that owns a segment's last chunk takes the
 //    newest token from k_new/v_new (its pool slot is masked in the loop),
 //    and writes it to its slot, which no other worker reads in this launch.
-#include "decode_common.h"
+#include "merge_body.h"
 
 namespace pa {
 namespace {
@@ -282,8 +282,8 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
 }
 
 // Merges the partial pieces of every segment that spans several workers.
-// One wave per (decode worker, group of kMergeHeads query heads of its
-// segment); each lane owns 4 dims of one head.  A worker that closes a split
+// One wave per (decode worker, group of merge_heads_per_wave query heads of
+// its segment); each lane owns 4 dims of one head.  A worker that closes a split
 // segment (its MergeRecord is valid) folds the pieces of workers first..w in
 // worker order, kBatch pieces per batch: the batch's accumulator rows and
 // (max, sum) pairs are all loaded before any is used, with a running max
@@ -292,7 +292,6 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
 // count, so results are deterministic.  Runs after
 // the decode launch in stream order: the partials are visible without any
 // in-kernel fence.
-constexpr int kMergeWaves = 4;   // waves per merge workgroup
 // Pieces loaded together: 8 keeps the merge's registers low for batches of
 // many segments, which have few pieces each.  When the workers average
 // kMergeWideFrom or more pieces per segment (few sequences and KV heads,
@@ -301,87 +300,11 @@ constexpr int kMergeWaves = 4;   // waves per merge workgroup
 constexpr int kMergeBatch = 8;
 constexpr int kMergeWideFrom = 16;
 
-template <int D>
-constexpr int merge_heads_per_wave() { return 64 / (D / 4); }
-
-template <typename T>
-__device__ __forceinline__ void store_out4(void* dst, const float* o, float inv);
-
-template <>
-__device__ __forceinline__ void store_out4<uint16_t>(void* dst, const float* o, float inv) {
-  uint2 r;
-  r.x = f32_to_bf16(o[0] * inv) | (f32_to_bf16(o[1] * inv) << 16);
-  r.y = f32_to_bf16(o[2] * inv) | (f32_to_bf16(o[3] * inv) << 16);
-  *reinterpret_cast<uint2*>(dst) = r;
-}
-
-template <>
-__device__ __forceinline__ void store_out4<float>(void* dst, const float* o, float inv) {
-  *reinterpret_cast<float4*>(dst) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-}
-
 template <typename T, int D, int kBatch>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArgs a, int workers) {
-  constexpr int LPH = D / 4;                       // lanes per head
-  constexpr int HPW = merge_heads_per_wave<D>();   // heads per wave
   const int lane = threadIdx.x % 64;
-  const int hps = a.heads_per_seg;
-  const int wpr = (hps + HPW - 1) / HPW;           // waves per record
   const int id = uniform((int)(blockIdx.x * kMergeWaves + threadIdx.x / 64));
-  const int w = id / wpr;
-  if (w >= workers) return;
-  typedef __attribute__((address_space(4))) const MergeRecord const_record;
-  const const_record* r = (const const_record*)a.records + w;   // scalar loads
-  if (!r->valid) return;
-  const int64_t first = r->first;
-  const int first_slot = r->first_slot;
-  const int g = (id - w * wpr) * HPW + lane / LPH;
-  if (g >= hps) return;   // no cross-lane work follows
-  const int d0 = (lane % LPH) * 4;
-  const int R = a.piece_rows;
-  constexpr int REC = D + kPartialExtra;   // acc[D], max, sum, pad
-  const int npieces = w - (int)first + 1;
-  float M = -INFINITY, S = 0.f;
-  float O[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < npieces; p0 += kBatch) {
-    float4 ob[kBatch];
-    float2 mb[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int p = p0 + b;
-      if (p < npieces) {
-        const int64_t slot = ((first + p) * 2 + (p == 0 ? first_slot : 0)) * R + g;
-        const float* rec = a.partials + slot * REC;
-        mb[b] = *reinterpret_cast<const float2*>(rec + D);
-        ob[b] = *reinterpret_cast<const float4*>(rec + d0);
-      } else {
-        mb[b] = make_float2(-INFINITY, 0.f);
-        ob[b] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-    float Mb = M;
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) Mb = fmaxf(Mb, mb[b].x);
-    const float Mu = Mb == -INFINITY ? 0.f : Mb;
-    const float alpha = fast_exp2(M - Mu);
-    S *= alpha;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) O[e] *= alpha;
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const float f = fast_exp2(mb[b].x - Mu);
-      S = fmaf(mb[b].y, f, S);
-      O[0] = fmaf(ob[b].x, f, O[0]);
-      O[1] = fmaf(ob[b].y, f, O[1]);
-      O[2] = fmaf(ob[b].z, f, O[2]);
-      O[3] = fmaf(ob[b].w, f, O[3]);
-    }
-    M = Mb;
-  }
-  const int head = r->head * hps + g;
-  char* out_row =
-      static_cast<char*>(a.out) + ((size_t)r->seq * a.num_q_heads + head) * (D * sizeof(T));
-  store_out4<T>(out_row + d0 * sizeof(T), O, 1.f / S);
+  merge_record_wave<T, D, kBatch>(a, workers, id, lane);
 }
 
 // The merge for segments of many pieces (few sequences and heads, where the

@@ -73,6 +73,38 @@ int validate_pairs(const int64_t* block_mapping, int64_t num_pairs, int64_t num_
   return PA_OK;
 }
 
+// PA_CHECK of pa_decode_shared's groups (lengths, tables and slots already
+// on the host): group_start runs from 0 to num_seqs without decreasing;
+// every prefix length lies in [0, context length] -- below it when the fused
+// append writes that sequence, so the new token is never shared -- and is
+// the same for every member of a group; and every member's table holds its
+// group's first member's blocks for the shared tokens.
+template <typename G>
+int validate_groups(const G& groups, const std::vector<int32_t>& lens,
+                    const std::vector<int32_t>& tables, const std::vector<int64_t>& slots,
+                    bool fused, int num_seqs, int max_blocks_per_seq, int block_size,
+                    hipStream_t st) {
+  std::vector<int32_t> gs, plen;
+  if (!copy_to_host(gs, groups.group_start, (size_t)groups.num_groups + 1, st)) return PA_ERR_HIP;
+  if (!copy_to_host(plen, groups.prefix_lens, (size_t)num_seqs, st)) return PA_ERR_HIP;
+  if (gs[0] != 0 || gs[(size_t)groups.num_groups] != num_seqs) return PA_ERR_INDEX;
+  for (int g = 0; g < groups.num_groups; ++g) {
+    const int lo = gs[(size_t)g], hi = gs[(size_t)g + 1];
+    if (hi < lo) return PA_ERR_INDEX;
+    for (int s = lo; s < hi; ++s) {
+      const int64_t P = plen[(size_t)s], L = lens[(size_t)s];
+      if (P < 0 || P > L || P != plen[(size_t)lo]) return PA_ERR_INDEX;
+      if (fused && slots[(size_t)s] >= 0 && P > L - 1) return PA_ERR_INDEX;
+      const int64_t nblk = (P + block_size - 1) / block_size;
+      for (int64_t j = 0; j < nblk; ++j)
+        if (tables[(size_t)s * max_blocks_per_seq + j] !=
+            tables[(size_t)lo * max_blocks_per_seq + j])
+          return PA_ERR_INDEX;
+    }
+  }
+  return PA_OK;
+}
+
 // Every entry of a host array of num_layers device pointers is non-null and
 // 16-byte aligned.
 template <typename P>
@@ -159,6 +191,29 @@ int default_workers_for_call(int dtype, int head_dim, int block_size, int max_bl
   int64_t cap = pieces * segments;
   cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;
   *out = cap < workers ? (int)(cap > 0 ? cap : 1) : workers;
+  return PA_OK;
+}
+
+// Default workers of a shared-prefix call: every worker of the shared
+// kernel resident at once, capped per segment like pa_decode with the tail
+// line's (sequence, KV head) segments.
+int default_workers_for_shared(int block_size, int max_blocks_per_seq, int num_seqs,
+                               int num_kv_heads, int* out) {
+  int cus = 0;
+  int st = current_device_cus(&cus);
+  if (st != PA_OK) return st;
+  int resident = 0;
+  if (pa::shared_resident_per_cu(block_size, &resident) != hipSuccess || resident <= 0)
+    return PA_ERR_HIP;
+  const int workers = cus * (resident < pa::kWavesPerCu ? resident : pa::kWavesPerCu);
+  const int64_t segments = (int64_t)num_seqs * num_kv_heads;
+  const int64_t chunks = (int64_t)max_blocks_per_seq * block_size / 16;
+  int64_t pieces = chunks / kChunksPerPiece;
+  pieces = pieces < kMinPiecesPerSegment ? kMinPiecesPerSegment : pieces;
+  pieces = pieces > kMaxPiecesPerSegment ? kMaxPiecesPerSegment : pieces;
+  int64_t cap = pieces * segments;
+  cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;
+  *out = cap < workers ? (int)(cap > 2 ? cap : 2) : workers;
   return PA_OK;
 }
 
@@ -352,13 +407,20 @@ namespace {
 // pa_decode's checks and launch.  `workspace` is the caller's workspace, or
 // -- for pa_decode_noalloc -- null, with `scratch` the current device's static
 // scratch array: the need is then checked against its size.
+// Groups of sequences that share a prefix (pa_decode_shared), or none.
+struct SharedGroups {
+  const int32_t* group_start;
+  int num_groups;
+  const int32_t* prefix_lens;
+};
+
 int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
                 const int32_t* block_tables, int max_blocks_per_seq,
                 const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                 int head_dim, int block_size, int64_t num_blocks, float scale,
                 const void* k_new, const void* v_new, const int64_t* slot_mapping,
                 void* workspace, size_t workspace_bytes, bool use_scratch, int num_workers,
-                int dtype, void* stream);
+                int dtype, void* stream, const SharedGroups* groups = nullptr);
 
 }  // namespace
 
@@ -428,7 +490,7 @@ int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
                 int head_dim, int block_size, int64_t num_blocks, float scale,
                 const void* k_new, const void* v_new, const int64_t* slot_mapping,
                 void* workspace, size_t workspace_bytes, bool use_scratch, int num_workers,
-                int dtype, void* stream) {
+                int dtype, void* stream, const SharedGroups* groups) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_workers < 0 ||
       !shape_ok(dtype, num_kv_heads, block_size, head_dim, num_blocks) ||
       num_q_heads % num_kv_heads != 0 || !(scale == scale))
@@ -443,16 +505,32 @@ int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
       (fused && (!aligned16(k_new) || !aligned16(v_new))))
     return PA_ERR_INVALID;
   if ((int64_t)num_seqs * num_q_heads > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  if (groups && (groups->num_groups < 0 || groups->num_groups > num_seqs ||
+                 (groups->num_groups > 0 && (!groups->group_start || !groups->prefix_lens))))
+    return PA_ERR_INVALID;
+  // The shared-prefix kernels serve bf16 head_dim 128 with 1..16 query heads
+  // per KV head; other shapes (and calls without groups) run plain decode,
+  // which computes the same attention.
+  const bool use_shared =
+      groups && groups->num_groups > 0 && pa::shared_supported(dtype, head_dim, group);
 
   int workers = num_workers;
   if (workers == 0) {
-    const int st = default_workers_for_call(dtype, head_dim, block_size, max_blocks_per_seq,
-                                            num_seqs, num_q_heads, num_kv_heads, &workers);
+    const int st = use_shared
+                       ? default_workers_for_shared(block_size, max_blocks_per_seq, num_seqs,
+                                                    num_kv_heads, &workers)
+                       : default_workers_for_call(dtype, head_dim, block_size, max_blocks_per_seq,
+                                                  num_seqs, num_q_heads, num_kv_heads, &workers);
     if (st != PA_OK) return st;
   }
-  const int group = num_q_heads / num_kv_heads;
+  if (use_shared && workers < 2) workers = 2;   // one worker per line at least
+  const pa::SharedLayout lay =
+      pa::shared_layout(workers, num_seqs, num_q_heads, num_kv_heads, head_dim);
   const size_t need =
-      pa::partials_bytes(workers, pa::decode_piece_rows(dtype, head_dim, group), head_dim);
+      use_shared ? lay.total
+                 : pa::partials_bytes(workers, pa::decode_piece_rows(dtype, head_dim, group),
+                                      head_dim);
   if (use_scratch) {
     if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
     const int sc = scratch_for_current_device(&workspace);
@@ -486,6 +564,11 @@ int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
         if (slots[(size_t)s] != want) return PA_ERR_INDEX;
       }
     }
+    if (groups && groups->num_groups > 0) {
+      const int vg = validate_groups(*groups, lens, tables, slots, fused != 0, num_seqs,
+                                     max_blocks_per_seq, block_size, st);
+      if (vg != PA_OK) return vg;
+    }
   }
 
   pa::DecodeArgs a;
@@ -506,6 +589,23 @@ int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
   a.num_kv_heads = num_kv_heads;
   a.group = group;
   a.scale_log2 = scale * 1.4426950408889634f;
+  if (use_shared) {
+    char* base = static_cast<char*>(workspace);
+    a.partials = reinterpret_cast<float*>(base + lay.partials);
+    pa::ShareArgs sh;
+    sh.group_start = groups->group_start;
+    sh.prefix_lens = groups->prefix_lens;
+    sh.loc_pre = reinterpret_cast<int32_t*>(base + lay.loc_pre);
+    sh.loc_tail = reinterpret_cast<int32_t*>(base + lay.loc_tail);
+    sh.res_pre = reinterpret_cast<float*>(base + lay.res_pre);
+    sh.res_tail = reinterpret_cast<float*>(base + lay.res_tail);
+    sh.num_groups = groups->num_groups;
+    sh.members_per_block = pa::kSharedPieceRows / group;
+    return pa::launch_decode_shared(a, sh, block_size, workers, st, tl_before, tl_after) ==
+                   hipSuccess
+               ? PA_OK
+               : PA_ERR_HIP;
+  }
   return pa::launch_decode(a, dtype, head_dim, block_size, workers, st, tl_before, tl_after) ==
                  hipSuccess
              ? PA_OK
@@ -513,6 +613,41 @@ int decode_impl(void* out, const void* q, void* k_cache, void* v_cache,
 }
 
 }  // namespace
+
+extern "C" int pa_decode_shared_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                               int head_dim, int num_workers, size_t* bytes) {
+  if (!bytes || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_workers < 0 || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_INVALID;
+  int workers = num_workers;
+  if (workers == 0) {
+    const int st = default_workers_for_current_device(&workers);
+    if (st != PA_OK) return st;
+  }
+  if (workers < 2) workers = 2;
+  const size_t shared =
+      pa::shared_layout(workers, num_seqs, num_q_heads, num_kv_heads, head_dim).total;
+  const size_t plain = pa::partials_bytes(workers, num_q_heads / num_kv_heads, head_dim);
+  *bytes = shared > plain ? shared : plain;
+  return PA_OK;
+}
+
+extern "C" int pa_decode_shared(void* out, const void* q, void* k_cache, void* v_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                int num_kv_heads, int head_dim, int block_size,
+                                int64_t num_blocks, float scale, const void* k_new,
+                                const void* v_new, const int64_t* slot_mapping,
+                                const int32_t* group_start, int num_groups,
+                                const int32_t* prefix_lens, void* workspace,
+                                size_t workspace_bytes, int num_workers, int dtype,
+                                void* stream) {
+  const SharedGroups groups{group_start, num_groups, prefix_lens};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     k_new, v_new, slot_mapping, workspace, workspace_bytes, false, num_workers,
+                     dtype, stream, &groups);
+}
 
 namespace pa {
 // Prefill with the context split over num_splits workgroups per row tile

@@ -80,6 +80,61 @@ inline size_t partials_bytes(int workers, int rows, int head_dim) {
          (size_t)workers * 2 * (size_t)rows * (size_t)partial_floats(head_dim) * sizeof(float);
 }
 
+// Decode with groups of sequences sharing a prefix (pa_decode_shared): what
+// the kernels read and write besides DecodeArgs.  A sequence's attention is
+// then the fold of two parts, each one result row (acc, max, sum) or a run of
+// split pieces: its shared prefix, computed once for the whole group by the
+// prefix line, and its own tail, computed by the tail line.  For every such
+// sequence and KV head a locator entry says where each part's pieces are:
+// (first worker, piece count, partial slot of the first piece, first row),
+// piece count 0 meaning "whole: the row in res_pre / res_tail".
+struct ShareArgs {
+  const int32_t* group_start;   // [num_groups + 1]: group g = sequences [gs[g], gs[g+1])
+  const int32_t* prefix_lens;   // [num_seqs]: leading tokens the sequence shares
+  int32_t* loc_pre;             // [num_kv_heads][num_seqs][4] locators of the prefix part
+  int32_t* loc_tail;            // [num_kv_heads][num_seqs][4] locators of the tail part
+  float* res_pre;               // [num_kv_heads][num_seqs][group][head_dim + 4]
+  float* res_tail;              // [num_kv_heads][num_seqs][group][head_dim + 4]
+  int num_groups;
+  int members_per_block;        // whole members per 16-row MFMA tile: 16 / group
+};
+
+// Rows of a partial piece slot in a shared-prefix decode: one 16-row MFMA
+// tile (the prefix line's members x query heads; the tail line uses `group`).
+constexpr int kSharedPieceRows = 16;
+
+// Workspace of pa_decode_shared: records, partial pieces (16 rows per slot),
+// the two locator arrays and the two result arrays, each 256-byte aligned.
+struct SharedLayout {
+  size_t records, partials, loc_pre, loc_tail, res_pre, res_tail, total;
+};
+inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline SharedLayout shared_layout(int workers, int num_seqs, int num_q_heads, int num_kv_heads,
+                                  int head_dim) {
+  SharedLayout L;
+  const size_t rec = (size_t)partial_floats(head_dim) * sizeof(float);
+  L.records = 0;
+  L.partials = records_bytes(workers);
+  L.loc_pre = L.partials + round256((size_t)workers * 2 * kSharedPieceRows * rec);
+  L.loc_tail = L.loc_pre + round256((size_t)num_kv_heads * num_seqs * 16);
+  L.res_pre = L.loc_tail + round256((size_t)num_kv_heads * num_seqs * 16);
+  L.res_tail = L.res_pre + round256((size_t)num_seqs * num_q_heads * rec);
+  L.total = L.res_tail + round256((size_t)num_seqs * num_q_heads * rec);
+  return L;
+}
+
+// The shared-prefix decode kernels run for bf16, head_dim 128 and 1..16 query
+// heads per KV head (the matrix-core body).
+bool shared_supported(int dtype, int head_dim, int group);
+// Launches the shared-prefix attention kernel (with `before`/`after`, when not
+// null, as its start and stop events) and its merge.  a.records/a.partials
+// and the ShareArgs arrays point into one SharedLayout workspace.
+hipError_t launch_decode_shared(const DecodeArgs& a, const ShareArgs& sh, int block_size,
+                                int workers, hipStream_t stream, hipEvent_t before,
+                                hipEvent_t after);
+// Resident shared-prefix decode workers (one-wave workgroups) per CU.
+hipError_t shared_resident_per_cu(int block_size, int* resident);
+
 // Launches the attention kernel (with `before`/`after`, when not null, as its
 // start and stop events) and then the merge kernel.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size,

@@ -102,6 +102,11 @@ class Workload:
     v_new: Optional[np.ndarray] = None
     slot_mapping: Optional[np.ndarray] = None
     block_mapping: Optional[np.ndarray] = None
+    # Groups of sequences sharing a prefix (pa_decode_shared): group g is the
+    # sequences group_start[g] .. group_start[g+1]-1; prefix_lens[s] tokens at
+    # the start of sequence s sit in blocks every member's table shares.
+    group_start: Optional[np.ndarray] = None
+    prefix_lens: Optional[np.ndarray] = None
     notes: dict = field(default_factory=dict)
 
     @property
@@ -122,6 +127,20 @@ class Workload:
     @property
     def has_append(self) -> bool:
         return self.slot_mapping is not None
+
+    @property
+    def kv_shared_read_bytes(self) -> Optional[int]:
+        """K/V bytes a decode step reads when each group's shared tokens are
+        read once: per group, its first member's shared tokens in whole
+        16-token chunks, plus every sequence's remaining tokens (None without
+        groups)."""
+        if self.group_start is None:
+            return None
+        lens = self.context_lens.astype(np.int64)
+        shared = (np.minimum(np.maximum(self.prefix_lens.astype(np.int64), 0), lens) // 16) * 16
+        firsts = self.group_start[:-1][np.diff(self.group_start) > 0]
+        tokens = int(shared[firsts].sum()) + int((lens - shared).sum())
+        return tokens * 2 * self.num_kv_heads * self.head_dim * elem_bytes(self.dtype)
 
 
 def _pool_size(need_blocks: int, factor: float = 1.25) -> int:
@@ -252,8 +271,84 @@ def _shared_prefix(name: str, seed: int, fork: bool, poison: bool) -> Workload:
     max_blocks = blocks_needed(max_len, bs)
     wl = _assemble(name, rng, BF16, 40, 40, 128, bs, num_blocks, mgr, list(range(b)),
                    decode_lens, max_blocks, slots, copies, poison)
+    # Each group's 8 samples share the prefix's 64 whole blocks (after the
+    # fork step's copies, the partial 65th block is private to each sample).
+    wl.group_start = np.arange(0, b + 1, per_group, dtype=np.int32)
+    wl.prefix_lens = np.full(b, prefix, dtype=np.int32)
     wl.notes["unique_tokens"] = int(groups * prefix + (decode_lens - prefix).sum()) if not fork \
         else int(sum(int(pre_lens[g * per_group]) for g in range(groups)) + b)
+    return wl
+
+
+def common_prefix_lens(tables: np.ndarray, lens: np.ndarray, group_start: np.ndarray,
+                       block_size: int, appended: bool) -> np.ndarray:
+    """Per sequence, the tokens its group shares physically: the leading
+    block-table entries equal in every member (within every member's blocks),
+    as tokens, at most the shortest member's length (less the token this
+    step appends, which is never shared)."""
+    out = np.zeros(len(lens), dtype=np.int32)
+    for g in range(len(group_start) - 1):
+        lo, hi = int(group_start[g]), int(group_start[g + 1])
+        if hi <= lo:
+            continue
+        lmin = int(lens[lo:hi].min()) - (1 if appended else 0)
+        nblk = blocks_needed(max(lmin, 0), block_size)
+        same = 0
+        while same < nblk and np.all(tables[lo:hi, same] == tables[lo, same]):
+            same += 1
+        out[lo:hi] = max(0, min(same * block_size, lmin))
+    return out
+
+
+def make_shared_groups(name: str, seed: int, dtype: str, num_q_heads: int, num_kv_heads: int,
+                       head_dim: int, block_size: int, group_sizes, prefix_tokens, tail_range,
+                       append: bool, poison: bool,
+                       rng: Optional[np.random.Generator] = None) -> Workload:
+    """Groups of sequences forked from a common parent: group g's parent holds
+    ``prefix_tokens[g]`` tokens when ``group_sizes[g]`` members are forked from
+    it; each member then grows a private tail of U[tail_range] tokens (the
+    first divergent write into a shared partial block copies it, as the host
+    block manager does), and with ``append`` the step appends one more token
+    per member (copying a still-shared tail block in the step itself:
+    ``block_mapping``).  ``prefix_lens`` are the tokens each group's members
+    still share physically after the step's copies.
+
+    Draw order: tails, pool permutation, then the values as ``_assemble``."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    sizes = [int(x) for x in group_sizes]
+    prefix = [int(x) for x in prefix_tokens]
+    b = sum(sizes)
+    tails = rng.integers(int(tail_range[0]), int(tail_range[1]) + 1, b)
+    # Blocks: each parent's prefix once, then per member its tail, a possible
+    # copy of a partial shared block and the step's append.
+    need = sum(blocks_needed(p, block_size) for p in prefix)
+    need += sum(blocks_needed(int(t) + 2, block_size) + 1 for t in tails)
+    num_blocks = max(1, _pool_size(need))
+    perm = rng.permutation(num_blocks)
+    mgr = BlockManager(num_blocks, block_size, free_order=perm)
+    seq = 0
+    for g, m in enumerate(sizes):
+        parent = seq
+        mgr.add_sequence(parent, prefix[g])
+        for i in range(1, m):
+            mgr.fork(parent, parent + i)
+        seq += m
+    for s in range(b):                      # private tails (copies happen before this step)
+        for _ in range(int(tails[s])):
+            mgr.append_slot(s)
+    slots, copies = ([], []) if append else (None, [])
+    if append:
+        for s in range(b):
+            slot, copy = mgr.append_slot(s)
+            slots.append(slot)
+            if copy is not None:
+                copies.append(copy)
+    lens = np.array([mgr.lengths[s] for s in range(b)], dtype=np.int64)
+    max_blocks = max(1, max(len(mgr.tables[s]) for s in range(b)))
+    wl = _assemble(name, rng, dtype, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                   mgr, list(range(b)), lens, max_blocks, slots, copies, poison)
+    wl.group_start = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    wl.prefix_lens = common_prefix_lens(wl.block_tables, lens, wl.group_start, block_size, append)
     return wl
 
 

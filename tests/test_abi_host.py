@@ -90,6 +90,56 @@ def test_decode_rejects_bad_scalars_before_any_hip_call(lib):
     assert decode_status(lib, b=0) == 0                   # nothing to do
 
 
+def shared_status(lib, gs=FAKE, ng=2, plen=FAKE, **kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tab=FAKE, mb=4, lens=FAKE, b=2, hq=8, hkv=8,
+                d=128, bs=16, nb=10, scale=0.1, kn=None, vn=None, sm=None, ws=None, wsb=0,
+                workers=64, dtype=1)
+    args.update(kw)
+    return lib.pa_decode_shared(args["out"], args["q"], args["k"], args["v"], args["tab"],
+                                args["mb"], args["lens"], args["b"], args["hq"], args["hkv"],
+                                args["d"], args["bs"], args["nb"], args["scale"], args["kn"],
+                                args["vn"], args["sm"], gs, ng, plen, args["ws"], args["wsb"],
+                                args["workers"], args["dtype"], None)
+
+
+def test_shared_decode_rejects_bad_arguments_before_any_hip_call(lib):
+    assert shared_status(lib, ng=-1) == 1
+    assert shared_status(lib, ng=3) == 1                  # more groups than sequences
+    assert shared_status(lib, gs=None) == 1
+    assert shared_status(lib, plen=None) == 1
+    assert shared_status(lib, d=96) == 2
+    assert shared_status(lib, hq=6, hkv=4) == 1
+    assert shared_status(lib) == 3                        # no workspace
+    assert shared_status(lib, ws=FAKE, wsb=4096) == 3     # too small for 64 workers
+    assert shared_status(lib, b=0, ng=0) == 0             # nothing to do
+
+
+def test_shared_workspace_size_covers_both_paths(lib):
+    sz = ctypes.c_size_t(0)
+    rec = 132 * 4
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert lib.pa_decode_shared_workspace_size(128, 40, 40, 128, 1024, ctypes.byref(sz)) == 0
+    want = (r256(1024 * 48) + r256(1024 * 2 * 16 * rec) + 2 * r256(40 * 128 * 16)
+            + 2 * r256(128 * 40 * rec))
+    assert sz.value == want
+    # fp32 head_dim 64 runs plain decode: the size still covers it
+    plain = ctypes.c_size_t(0)
+    assert lib.pa_decode_workspace_size(3, 64, 1, 64, 7, ctypes.byref(plain)) == 0
+    assert lib.pa_decode_shared_workspace_size(3, 64, 1, 64, 7, ctypes.byref(sz)) == 0
+    assert sz.value >= plain.value
+    assert lib.pa_decode_shared_workspace_size(4, 6, 4, 64, 8, ctypes.byref(sz)) == 1
+
+
+def test_noalloc_rejects_a_need_beyond_the_scratch_before_any_hip_call(lib):
+    # 200,000 workers of 8 query heads per KV head need 1.7 GB of partials.
+    st = lib.pa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 128, 16, 10,
+                               0.1, None, None, None, 200000, 1, None)
+    assert st == 3
+    st = lib.pa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 96, 16, 10,
+                               0.1, None, None, None, 8, 1, None)
+    assert st == 2
+
+
 def test_append_and_copy_reject_bad_scalars(lib):
     assert lib.pa_append_kv(None, None, None, None, None, 0, 10, 8, 16, 128, 1, None) == 0
     assert lib.pa_append_kv(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 8, 16, 96, 1, None) == 2
