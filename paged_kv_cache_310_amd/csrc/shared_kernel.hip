@@ -439,6 +439,11 @@ __device__ __forceinline__ void prefix_body(const DecodeArgs& a, const ShareArgs
 
 // ---------------------------------------------------------------------------
 // The launch: both lines, workers shared out by work units.
+// Measured: with tail segments of 8.6 chunks (the steady shared-prefix
+// batch) and of 1 chunk (the fork batch), the division that ran fastest
+// weighted them about 10.6 and 3.8 prefix chunk times; a line through both.
+constexpr int kTailChunkTime10 = 9;
+constexpr int kTailSegTime10 = 29;
 template <int BS>
 // One-wave workgroups, one per SIMD: the kernel holds both worker loops.
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(1)))
@@ -464,9 +469,16 @@ void decode_shared_kernel(const DecodeArgs a, const ShareArgs sh) {
   int64_t tw, tu, pw, pu;
   tail_line_totals(lds.split, lens, sh.prefix_lens, B, a.seg_cost, lane, tw, tu);
   prefix_line_totals(sh, lens, B, a.seg_cost, lane, pw, pu);
-  const int64_t UT = tu * HKV, UP = pu * HKV;
-  // Prefix workers: the prefix line's share of the units, at least one for
-  // each line that has work.
+  const int64_t UP = pu * HKV;
+  // Workers are divided by the lines' estimated times, in tenths of a prefix
+  // chunk's time: a tail chunk kTailChunkTime10 (a segment's last chunk is
+  // partial), a tail segment kTailSegTime10 besides its chunks (its end also
+  // writes its result row and locator, and with the fused append the new
+  // token's rows).
+  const int64_t tail_segs = (tu - tw) / a.seg_cost;
+  const int64_t UT = (kTailChunkTime10 * tw + kTailSegTime10 * tail_segs) * HKV / 10;
+  // Prefix workers: the prefix line's share, at least one for each line that
+  // has work.
   int wp = 0;
   if (UP > 0 && UT == 0) {
     wp = nworkers;
@@ -497,35 +509,41 @@ void decode_shared_kernel(const DecodeArgs a, const ShareArgs sh) {
 // prefix, as in pa_decode), then one wave per (sequence, two query heads)
 // folding the prefix and tail parts of sequences with a shared prefix.
 
-// Folds one part (its locator, its result rows) of query head hh of KV head
-// kvh, sequence s into (M, S, O).  A locator naming pieces outside the
-// workspace (only an out-of-contract call can leave one) is ignored.
-__device__ __forceinline__ void fold_part(const DecodeArgs& a, int workers, const int32_t* loc,
-                                          const float* res, int kvh, int s, int hh, int d0,
-                                          float& M, float& S, float* O) {
+// Folds one (max, sum, acc) record into the running (M, S, O).
+__device__ __forceinline__ void fold_one(float2 ms, float4 o, float& M, float& S, float* O) {
+  const float Mb = fmaxf(M, ms.x);
+  const float Mu = Mb == -INFINITY ? 0.f : Mb;
+  const float alpha = fast_exp2(M - Mu);
+  const float f = fast_exp2(ms.x - Mu);
+  S = fmaf(ms.y, f, S * alpha);
+  O[0] = fmaf(o.x, f, O[0] * alpha);
+  O[1] = fmaf(o.y, f, O[1] * alpha);
+  O[2] = fmaf(o.z, f, O[2] * alpha);
+  O[3] = fmaf(o.w, f, O[3] * alpha);
+  M = Mb;
+}
+
+// Folds the split pieces a locator names (row `row` of each piece) into the
+// running (M, S, O), kBatch pieces' loads in flight at once.  A locator that
+// names pieces outside the workspace (only an out-of-contract call can leave
+// one) is ignored.
+__device__ __forceinline__ void fold_pieces(const DecodeArgs& a, int workers, int4 e, int row,
+                                            int d0, float& M, float& S, float* O) {
   constexpr int REC = kD + kPartialExtra;
   constexpr int kBatch = 8;
-  const int B = a.num_seqs, G = a.group;
-  const int4 e = *reinterpret_cast<const int4*>(loc + ((int64_t)kvh * B + s) * 4);
-  const int first = e.x, count = e.y, slot0 = e.z, row = e.w + hh;
-  int npieces = count;
-  if (count <= 0) {
-    npieces = 1;
-  } else if (first < 0 || count > workers || first > workers - count || (slot0 & ~1) ||
-             row < 0 || row >= kSharedPieceRows) {
+  const int first = e.x, count = e.y, slot0 = e.z;
+  if (first < 0 || count > workers || first > workers - count || (slot0 & ~1) || row < 0 ||
+      row >= kSharedPieceRows)
     return;
-  }
-  for (int p0 = 0; p0 < npieces; p0 += kBatch) {
+  for (int p0 = 0; p0 < count; p0 += kBatch) {
     float4 ob[kBatch];
     float2 mbv[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const int p = p0 + b;
-      if (p < npieces) {
-        const float* rec =
-            count <= 0 ? res + (((int64_t)kvh * B + s) * G + hh) * REC
-                       : a.partials + (((int64_t)(first + p) * 2 + (p == 0 ? slot0 : 0)) *
-                                           a.piece_rows + row) * REC;
+      if (p < count) {
+        const float* rec = a.partials + (((int64_t)(first + p) * 2 + (p == 0 ? slot0 : 0)) *
+                                             a.piece_rows + row) * REC;
         mbv[b] = *reinterpret_cast<const float2*>(rec + kD);
         ob[b] = *reinterpret_cast<const float4*>(rec + d0);
       } else {
@@ -558,6 +576,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_shared_kernel(const De
                                                                         const ShareArgs sh,
                                                                         int workers,
                                                                         int record_waves) {
+  constexpr int REC = kD + kPartialExtra;
   const int lane = threadIdx.x % 64;
   const int id = uniform((int)(blockIdx.x * kMergeWaves + threadIdx.x / 64));
   if (id < record_waves) {
@@ -565,22 +584,43 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_shared_kernel(const De
     return;
   }
   constexpr int HPW = merge_heads_per_wave<kD>();   // 2 heads of 32 lanes x 4 dims
-  const int HQ = a.num_q_heads;
+  const int B = a.num_seqs, HQ = a.num_q_heads, G = a.group;
   const int per_seq = (HQ + HPW - 1) / HPW;
   const int v = id - record_waves;
   const int s = v / per_seq;
-  if (s >= a.num_seqs) return;
+  if (s >= B) return;
   const int hq = (v - s * per_seq) * HPW + lane / 32;
   if (hq >= HQ) return;   // no cross-lane work follows
-  const int L = a.context_lens[s];
-  const int c0 = shared_chunks(L, sh.prefix_lens[s]);
-  if (c0 == 0) return;    // no shared prefix: written by the attention or record merge
-  const int kvh = hq / a.group, hh = hq - kvh * a.group;
+  const int kvh = hq / G, hh = hq - kvh * G;
   const int d0 = (lane % 32) * 4;
+  // Everything the common case needs, in one round of loads: the lengths,
+  // both locators and both parts' result rows (read whether or not this
+  // call wrote them; used only when the locator says so).
+  const int64_t idx = (int64_t)kvh * B + s;
+  const int L = a.context_lens[s];
+  const int P = sh.prefix_lens[s];
+  const int4 ep = *reinterpret_cast<const int4*>(sh.loc_pre + idx * 4);
+  const int4 et = *reinterpret_cast<const int4*>(sh.loc_tail + idx * 4);
+  const float* rp = sh.res_pre + (idx * G + hh) * REC;
+  const float* rt = sh.res_tail + (idx * G + hh) * REC;
+  const float2 mp = *reinterpret_cast<const float2*>(rp + kD);
+  const float4 op = *reinterpret_cast<const float4*>(rp + d0);
+  const float2 mt = *reinterpret_cast<const float2*>(rt + kD);
+  const float4 ot = *reinterpret_cast<const float4*>(rt + d0);
+  const int c0 = shared_chunks(L, P);
+  if (c0 == 0) return;    // no shared prefix: written by the attention or record merge
   float M = -INFINITY, S = 0.f;
   float O[4] = {0.f, 0.f, 0.f, 0.f};
-  fold_part(a, workers, sh.loc_pre, sh.res_pre, kvh, s, hh, d0, M, S, O);
-  if (chunks_of(L) - c0 > 0) fold_part(a, workers, sh.loc_tail, sh.res_tail, kvh, s, hh, d0, M, S, O);
+  if (ep.y <= 0)
+    fold_one(mp, op, M, S, O);
+  else
+    fold_pieces(a, workers, ep, ep.w + hh, d0, M, S, O);
+  if (chunks_of(L) - c0 > 0) {
+    if (et.y <= 0)
+      fold_one(mt, ot, M, S, O);
+    else
+      fold_pieces(a, workers, et, et.w + hh, d0, M, S, O);
+  }
   char* out_row = static_cast<char*>(a.out) + ((size_t)s * HQ + hq) * kRow;
   store_out4<uint16_t>(out_row + d0 * 2, O, 1.f / S);
 }
