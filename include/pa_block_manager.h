@@ -123,6 +123,20 @@ int pa_bm_length(const pa_bm* bm, int64_t seq, int64_t* length);
 int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int64_t n, int64_t max_blocks,
                        int32_t pad, int32_t* tables, int32_t* context_lens);
 
+/* The leading tokens each sequence shares physically with the rest of its
+ * group -- what pa_decode_shared (pa.h) takes as prefix_lens.  The n
+ * sequences seqs[0..n) form num_groups groups of consecutive entries,
+ * group g = seqs[group_start[g] .. group_start[g+1]) (group_start[0] = 0,
+ * non-decreasing, group_start[num_groups] = n).  For a group of two or more,
+ * every member gets (the number of leading block-table entries that are the
+ * same physical block in every member) * block_size, at most the shortest
+ * member's length; a group of one gets 0.  Call it after the step's
+ * pa_bm_append_slots: every sequence's newest token then sits in a block of
+ * its own (a shared partly filled tail block is copied before the write), so
+ * it is never counted as shared.  Writes prefix_lens[0..n). */
+int pa_bm_shared_prefix(const pa_bm* bm, const int64_t* seqs, int64_t n,
+                        const int64_t* group_start, int64_t num_groups, int32_t* prefix_lens);
+
 /* Reference count of one block. */
 int pa_bm_refcount(const pa_bm* bm, int64_t block, int64_t* refcount);
 

@@ -6,15 +6,17 @@ blocks): 16 requests, each a 1000-token prompt (so its last prompt block is
 partly filled) searched with 8 beams.  Every step keeps 2 seeded survivors per
 request, forks each back to 8 beams (one batched free and one batched fork
 call for all requests), asks the host block manager (libpabm.so) for the
-slots and copy-on-write pairs, and runs pa_copy_blocks and a fused
-append + pa_decode for all 128 beams.
+slots, the copy-on-write pairs and what each request's beams share
+(pa_bm_shared_prefix), and runs pa_copy_blocks and a fused append +
+pa_decode_shared for all 128 beams, each request's beams one group
+(``--plain``: pa_decode).
 
 Reported per step: wall-clock time of the whole step (host manager + uploads
 + device work), the manager's share, device time of the copy and of the
 decode (HIP events on the stream the calls use, sampled every 10th step so the
 events do not slow the loop), copies per step, and the decode's KV read rate
 in algorithmic bytes (every cached token's K and V rows of every beam, shared
-blocks counted once per beam that reads them).
+blocks counted once per beam that reads them -- the logical bytes).
 """
 
 from __future__ import annotations
@@ -35,6 +37,9 @@ def _args():
     p.add_argument("--prompt", type=int, default=1000)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--plain", dest="shared", action="store_false",
+                   help="decode with pa_decode instead of pa_decode_shared (each request's "
+                        "beams as one group)")
     return p.parse_args()
 
 
@@ -55,7 +60,10 @@ def main():
     kn = torch.randn(b, hkv, d, device=dev).bfloat16()
     vn = torch.randn(b, hkv, d, device=dev).bfloat16()
     out = torch.empty_like(q)
-    ws = pa.decode_workspace(dev, pa.pa_decode_workspace_size(b, hq, hkv, d))
+    ws = pa.decode_workspace(dev, pa.pa_decode_shared_workspace_size(b, hq, hkv, d))
+    # Each request's beams are one group: they share the prompt's blocks.
+    starts = np.arange(0, b + 1, a.width, dtype=np.int64)
+    starts_d = torch.from_numpy(starts.astype(np.int32)).to(dev)
     scale = 1.0 / np.sqrt(d)
 
     mgr = KVBlockManager(nb, bs, free_order=rng.permutation(nb))
@@ -97,6 +105,7 @@ def main():
         mgr.fork_many(parents, children)
         slots, copies = mgr.append_slots(live)
         tables, lens = mgr.block_tables(live, max_blocks=max_blocks)
+        prefix = mgr.shared_prefix(live, starts) if a.shared else None
         t1 = time.perf_counter()
         slots_d = torch.from_numpy(slots).to(dev)
         tables_d = torch.from_numpy(tables).to(dev)
@@ -108,8 +117,13 @@ def main():
             pa.pa_copy_blocks(k, v, copies_d)
         if sample:
             ev[1].record()
-        pa.pa_decode(q, k, v, tables_d, lens_d, float(scale), out=out, k_new=kn, v_new=vn,
-                     slot_mapping=slots_d, workspace=ws)
+        if a.shared:
+            pa.pa_decode_shared(q, k, v, tables_d, lens_d, float(scale), starts_d,
+                                torch.from_numpy(prefix).to(dev), out=out, k_new=kn, v_new=vn,
+                                slot_mapping=slots_d, workspace=ws)
+        else:
+            pa.pa_decode(q, k, v, tables_d, lens_d, float(scale), out=out, k_new=kn, v_new=vn,
+                         slot_mapping=slots_d, workspace=ws)
         if sample:
             ev[2].record()
             ev[2].synchronize()
@@ -135,6 +149,8 @@ def main():
         "metric": "beam-search churn step, microseconds (lower is better)",
         "workload": f"llama13b heads, {a.requests} requests x {a.width} beams, prompt "
                     f"{a.prompt}, keep {a.keep}",
+        "decode": "pa_decode_shared (each request's beams one group)" if a.shared
+                  else "pa_decode",
         "steps": a.steps, "pool_blocks": nb,
         "step_us_wall": round(wall, 1),
         "manager_us": round(float(np.median(rec["mgr"])), 1),

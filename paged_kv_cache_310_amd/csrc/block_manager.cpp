@@ -26,6 +26,7 @@
 #include <memory>
 #include <new>
 #include <unordered_map>
+#include <algorithm>
 #include <vector>
 
 namespace {
@@ -474,6 +475,48 @@ int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int64_t n, int64_t 
     for (int64_t j = 0; j < nb; ++j) row[j] = (int32_t)s.table[j];
     for (int64_t j = nb; j < max_blocks; ++j) row[j] = pad;
     if (context_lens != nullptr) context_lens[i] = (int32_t)s.length;
+  }
+  return PA_BM_OK;
+}
+
+int pa_bm_shared_prefix(const pa_bm* bm, const int64_t* seqs, int64_t n,
+                        const int64_t* group_start, int64_t num_groups, int32_t* prefix_lens) {
+  if (bm == nullptr || n < 0 || num_groups < 0 ||
+      (n > 0 && (seqs == nullptr || prefix_lens == nullptr)) || group_start == nullptr)
+    return PA_BM_INVALID;
+  if (group_start[0] != 0 || group_start[num_groups] != n) return PA_BM_INVALID;
+  for (int64_t g = 0; g < num_groups; ++g)
+    if (group_start[g + 1] < group_start[g]) return PA_BM_INVALID;
+  std::vector<const Sequence*> members((size_t)n);
+  for (int64_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return PA_BM_UNKNOWN_SEQ;
+    members[(size_t)i] = &it->second;
+  }
+  for (int64_t g = 0; g < num_groups; ++g) {
+    const int64_t lo = group_start[g], hi = group_start[g + 1];
+    int64_t shared = 0;
+    if (hi - lo >= 2) {
+      // Leading blocks every member holds (the same physical block), and at
+      // most the shortest member's length in tokens.
+      int64_t blocks = INT64_MAX, min_len = INT64_MAX;
+      for (int64_t i = lo; i < hi; ++i) {
+        blocks = std::min<int64_t>(blocks, (int64_t)members[(size_t)i]->table.size());
+        min_len = std::min<int64_t>(min_len, members[(size_t)i]->length);
+      }
+      const std::vector<int64_t>& first = members[(size_t)lo]->table;
+      int64_t same = 0;
+      while (same < blocks) {
+        bool all = true;
+        for (int64_t i = lo + 1; i < hi && all; ++i)
+          all = members[(size_t)i]->table[(size_t)same] == first[(size_t)same];
+        if (!all) break;
+        ++same;
+      }
+      shared = std::min<int64_t>(same * bm->block_size, min_len);
+    }
+    if (shared > INT32_MAX) return PA_BM_INVALID;
+    for (int64_t i = lo; i < hi; ++i) prefix_lens[i] = (int32_t)shared;
   }
   return PA_BM_OK;
 }

@@ -50,11 +50,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int offset) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
 }
-// The same load with the non-temporal hint (`nt`: no reuse expected).  Used
-// for V tiles: with the V stream marked non-temporal the long-context batch
-// reads 10% faster; K stays cacheable, so K rows of prefix blocks that
-// several sequences share still hit in L2 (marking both streams loses 17% on
-// a shared-prefix batch, V alone 3.5%).
+// The same load with the non-temporal hint (`nt`: no reuse expected).  The
+// vector kernel reads both K and V tiles this way (+10% for V, then +0.9% on
+// the long-context and +1.5% on the OPT-shaped batch for K as well); a batch
+// whose sequences share prefix blocks re-reads them through L2 and loses 16%
+// with it -- pa_decode_shared reads such blocks once instead.  The
+// matrix-core loops keep K cacheable (non-temporal K measured 2.4% slower
+// there; the shared-prefix line re-reads a tile once per row block).
 __device__ __forceinline__ u32x4 load16_stream(__amdgpu_buffer_rsrc_t r, int offset) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 2);
 }

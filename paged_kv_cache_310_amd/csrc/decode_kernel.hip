@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
         tile_rsrc(static_cast<const char*>(a.v_cache) + off, kChunk * ROW);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      t.k[i] = load16(kr, i * 1024 + lane * 16);
+      t.k[i] = load16_stream(kr, i * 1024 + lane * 16);
       t.v[i] = load16_stream(vr, i * 1024 + lane * 16);
     }
     if (drain) {

@@ -71,6 +71,7 @@ def _load():
         lib.pa_bm_length.argtypes = [vp, i64, p64]
         lib.pa_bm_block_tables.argtypes = [vp, p64, i64, i64, ctypes.c_int32, p32, p32]
         lib.pa_bm_refcount.argtypes = [vp, i64, p64]
+        lib.pa_bm_shared_prefix.argtypes = [vp, p64, i64, p64, i64, p32]
         lib.pa_bm_get_stats.argtypes = [vp, ctypes.POINTER(_Stats)]
         lib.pa_bm_check.argtypes = [vp]
         lib.pa_bm_fnv1a64.argtypes = [ctypes.c_uint64, vp, i64]
@@ -78,7 +79,8 @@ def _load():
         lib.pa_bm_status_string.argtypes = [i32]
         lib.pa_bm_status_string.restype = ctypes.c_char_p
         for f in ("pa_bm_create", "pa_bm_add_sequence", "pa_bm_append_slots", "pa_bm_fork",
-                  "pa_bm_free_sequence", "pa_bm_fork_many", "pa_bm_free_many", "pa_bm_length", "pa_bm_block_tables", "pa_bm_refcount",
+                  "pa_bm_free_sequence", "pa_bm_fork_many", "pa_bm_free_many", "pa_bm_length",
+                  "pa_bm_block_tables", "pa_bm_refcount", "pa_bm_shared_prefix",
                   "pa_bm_get_stats", "pa_bm_check"):
             getattr(lib, f).restype = i32
         _lib = lib
@@ -207,6 +209,18 @@ class KVBlockManager:
         _call("pa_bm_block_tables", _load().pa_bm_block_tables(
             self._h, _p64(s), s.size, int(max_blocks), int(pad), _p32(tables), _p32(lens)))
         return tables, lens
+
+    def shared_prefix(self, seqs: Sequence[int], group_start: Sequence[int]) -> np.ndarray:
+        """int32 [n]: the leading tokens each sequence shares physically with
+        the rest of its group (groups are runs of ``seqs``:
+        ``group_start[g] .. group_start[g+1]``; a group of one shares 0) --
+        ``prefix_lens`` for ``pa_decode_shared``."""
+        s = _i64(seqs)
+        gs = _i64(group_start)
+        out = np.empty(s.size, dtype=np.int32)
+        _call("pa_bm_shared_prefix", _load().pa_bm_shared_prefix(
+            self._h, _p64(s), s.size, _p64(gs), gs.size - 1, _p32(out)))
+        return out
 
     def refcount(self, block: int) -> int:
         out = ctypes.c_int64(0)

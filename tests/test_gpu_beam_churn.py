@@ -4,7 +4,9 @@ the device operations through many fork / prune / copy-on-write steps.
 Each step prunes the live beams to a few seeded survivors, forks each back up
 to the beam width, asks the manager for every beam's next slot and the
 copy-on-write pairs, runs the layer-batched copy and append (or the fused
-append inside pa_decode) and decodes every layer.  Checked each step:
+append inside pa_decode) and decodes every layer -- layer 1 with
+pa_decode_shared, the beams grouped by the blocks they share (the manager's
+pa_bm_shared_prefix).  Checked each step:
   * every layer's pools are bit-identical to pools the oracle maintains with
     the same copies and appends;
   * every beam's attention output matches attention (oracle, fp64) over that
@@ -124,12 +126,23 @@ def test_beam_churn_matches_oracle(hq, hkv, bs):
         max_blocks = max(-(-len(history[s][0][0]) // bs) for s in live)
         tables, lens = mgr.block_tables(live, max_blocks=max_blocks)
         tables_d, lens_d = to_dev(tables), to_dev(lens)
+        # Layer 1 decodes with the beams grouped by what they share (the
+        # manager's shared prefix): all beams as one group on even steps, each
+        # survivor's family as a group on odd steps.
+        starts = [0, len(live)] if step % 2 == 0 else list(range(0, len(live) + 1, width // keep))
+        prefix = mgr.shared_prefix(live, starts)
+        assert prefix.max() > 0 and (prefix < lens).all()
         for l in range(layers):
             fused = fused0 and l == 0
-            out = pa.pa_decode(to_dev(q[l]), dev_k[l], dev_v[l], tables_d, lens_d, float(scale),
-                               k_new=kn_d[l] if fused else None,
-                               v_new=vn_d[l] if fused else None,
-                               slot_mapping=slots_d if fused else None)
+            if l == 1:
+                out = pa.pa_decode_shared(to_dev(q[l]), dev_k[l], dev_v[l], tables_d, lens_d,
+                                          float(scale), to_dev(np.asarray(starts, np.int32)),
+                                          to_dev(prefix))
+            else:
+                out = pa.pa_decode(to_dev(q[l]), dev_k[l], dev_v[l], tables_d, lens_d,
+                                   float(scale), k_new=kn_d[l] if fused else None,
+                                   v_new=vn_d[l] if fused else None,
+                                   slot_mapping=slots_d if fused else None)
             torch.cuda.synchronize()
             assert np.array_equal(to_host(dev_k[l]), host_k[l]), f"step {step} K pool layer {l}"
             assert np.array_equal(to_host(dev_v[l]), host_v[l]), f"step {step} V pool layer {l}"

@@ -130,6 +130,65 @@ def test_batch_of_siblings_copies_a_shared_tail_once():
     m2.check()
 
 
+def test_shared_prefix_counts_blocks_every_member_holds():
+    # three forks of a 40-token sequence (16-token blocks: 2 full + 1 partial)
+    m = kvb.KVBlockManager(12, 16, free_order=range(12))
+    m.add_sequence(0, 40)
+    m.fork(0, 1)
+    m.fork(0, 2)
+    m.add_sequence(3, 20)
+    # before any write all three hold all three blocks: the whole 40 tokens
+    assert m.shared_prefix([0, 1, 2, 3], [0, 3, 4]).tolist() == [40, 40, 40, 0]
+    # the step's appends copy the shared partial block for two of them
+    m.append_slots([0, 1, 2, 3])
+    assert m.shared_prefix([0, 1, 2, 3], [0, 3, 4]).tolist() == [32, 32, 32, 0]
+    # one member growing a private tail does not change what the others share
+    for _ in range(30):
+        m.append_slots([1])
+    assert m.shared_prefix([0, 1, 2], [0, 3]).tolist() == [32, 32, 32]
+    # groups of two within the same family: still the common blocks
+    assert m.shared_prefix([2, 0, 1], [0, 2, 3]).tolist() == [32, 32, 0]
+    with pytest.raises(kvb.BlockManagerError):
+        m.shared_prefix([0, 1], [0, 3])          # group_start past n
+    with pytest.raises(kvb.BlockManagerError):
+        m.shared_prefix([0, 99], [0, 2])         # unknown sequence
+
+
+def test_shared_prefix_agrees_with_tables_on_random_families():
+    """For random fork/append histories, the manager's shared prefix equals the
+    common leading table entries (capped at the shortest member) computed from
+    its own block tables."""
+    rng = np.random.default_rng(7)
+    for trial in range(25):
+        bs = int(rng.choice([16, 32]))
+        m = kvb.KVBlockManager(4000, bs, free_order=rng.permutation(4000))
+        seqs, starts, next_id = [], [0], 0
+        for g in range(int(rng.integers(1, 6))):
+            members = int(rng.integers(1, 7))
+            root = next_id
+            m.add_sequence(root, int(rng.integers(0, 300)))
+            fam = [root]
+            next_id += 1
+            for _ in range(members - 1):
+                m.fork(int(rng.choice(fam)), next_id)
+                fam.append(next_id)
+                next_id += 1
+            for _ in range(int(rng.integers(0, 40))):
+                m.append_slots([int(x) for x in rng.choice(fam, size=int(rng.integers(1, len(fam) + 1)), replace=False)])
+            seqs.extend(fam)
+            starts.append(len(seqs))
+        got = m.shared_prefix(seqs, starts)
+        tables, lens = m.block_tables(seqs, max_blocks=64)
+        want = wl.common_prefix_lens(tables, lens, np.asarray(starts), bs, appended=False)
+        for g in range(len(starts) - 1):
+            lo, hi = starts[g], starts[g + 1]
+            if hi - lo == 1:
+                assert got[lo] == 0
+            else:
+                assert got[lo:hi].tolist() == want[lo:hi].tolist(), (trial, g)
+        m.check()
+
+
 def _tokens(rng, n, vocab=50000):
     return rng.integers(0, vocab, size=n).astype(np.int32)
 
