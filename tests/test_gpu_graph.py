@@ -67,6 +67,84 @@ def test_decode_step_replays_in_a_graph(hq, hkv):
         assert same(k, ref_k) and same(v, ref_v), f"replay {r}: pools differ"
 
 
+def _replay_and_check(step, outputs, pools, pools0):
+    """Eager result of step(), then capture it and replay it 5 times, with the
+    pools reset and the outputs cleared (and host synchronization) between
+    replays; every replay must equal the eager result bit for bit."""
+    for p, p0 in zip(pools, pools0):
+        p.copy_(p0)
+    step()
+    torch.cuda.synchronize()
+    ref_out = [o.clone() for o in outputs]
+    ref_pools = [p.clone() for p in pools]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(5):
+        for o in outputs:
+            o.fill_(0)
+        for p, p0 in zip(pools, pools0):
+            p.copy_(p0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, ro in zip(outputs, ref_out):
+            assert same(o, ro), f"replay {r}: output differs"
+        for p, rp in zip(pools, ref_pools):
+            assert same(p, rp), f"replay {r}: pools differ"
+
+
+def test_shared_decode_step_replays_in_a_graph():
+    """A fork step of pa_decode_shared (copy-on-write copies, then the
+    shared-prefix attention kernel with the append fused, then its merge)."""
+    import paged_kv_cache_310_amd as pa
+    say("graph shared decode")
+    # No private tails yet: each member's append copies its group's partial
+    # last block in the step itself.
+    w = wl.make_shared_groups("graph_shared", 66, wl.BF16, 16, 2, 128, 16, [4, 1, 3],
+                              [300, 40, 1000], (0, 0), True, poison=True)
+    assert w.block_mapping is not None
+    q, k, v = to_dev(w.q), to_dev(w.k_cache), to_dev(w.v_cache)
+    tab, lens = to_dev(w.block_tables), to_dev(w.context_lens)
+    kn, vn, slots, pairs = to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping), \
+        to_dev(w.block_mapping)
+    gs, pl = to_dev(w.group_start), to_dev(w.prefix_lens)
+    ws = torch.empty(pa.pa_decode_shared_workspace_size(w.num_seqs, 16, 2, 128),
+                     dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+
+    def step():
+        pa.pa_copy_blocks(k, v, pairs)
+        pa.pa_decode_shared(q, k, v, tab, lens, float(w.scale), gs, pl, out=out, k_new=kn,
+                            v_new=vn, slot_mapping=slots, workspace=ws)
+
+    _replay_and_check(step, [out], [k, v], [k.clone(), v.clone()])
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 2)], ids=["mha", "gqa8"])
+def test_noalloc_decode_replays_in_a_graph(hq, hkv):
+    """pa_decode_noalloc (workspace in the library's static scratch array)."""
+    import paged_kv_cache_310_amd as pa
+    say("graph noalloc decode", hq, hkv)
+    w = wl.make_simple("graph_noalloc", 67 + hq, wl.BF16, hq, hkv, 128, 16,
+                       [1, 17, 300, 1000, 40, 2049], append=True, poison=True)
+    q, k, v = to_dev(w.q), to_dev(w.k_cache), to_dev(w.v_cache)
+    tab, lens = to_dev(w.block_tables), to_dev(w.context_lens)
+    kn, vn, slots = to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping)
+    out = torch.empty_like(q)
+
+    def step():
+        pa.pa_decode_noalloc(q, k, v, tab, lens, float(w.scale), out=out, k_new=kn, v_new=vn,
+                             slot_mapping=slots)
+
+    _replay_and_check(step, [out], [k, v], [k.clone(), v.clone()])
+
+
 def test_prefill_replays_in_a_graph():
     import paged_kv_cache_310_amd as pa
     say("graph prefill")

@@ -18,7 +18,7 @@ import torch
 
 from paged_kv_cache_310_amd import workloads as wl
 from _gpu_util import (DeviceWorkload, assert_attention_close, oracle_decode, oracle_pools,
-                       out_f64, to_dev, to_host)
+                       out_f64, sample_rows, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,6 +121,60 @@ def test_shared_other_shapes_run_plain_decode(dtype, d):
     w = wl.make_shared_groups("shared_plain", 4300, dtype, 8, 4, d, 16, [4, 2], [300, 40],
                               (0, 60), True, poison=True)
     check(w)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 2)], ids=["gqa8-1kv", "gqa8-2kv"])
+def test_shared_more_sequences_than_the_length_cache(hq, hkv):
+    """5,000 sequences in groups of 1..6: both lines' splits cache 4,096
+    lengths in LDS and read the rest from memory; prefixes of 0..69 tokens,
+    tails of 0..20, one appended token each."""
+    rng = np.random.default_rng(4600 + hq)
+    sizes = []
+    while sum(sizes) < 5000:
+        sizes.append(int(rng.integers(1, 7)))
+    sizes[-1] -= sum(sizes) - 5000
+    assert sizes[-1] >= 1 and sum(sizes) == 5000
+    prefix = rng.integers(0, 70, len(sizes))
+    w = wl.make_shared_groups("shared_many", 4600 + hq, wl.BF16, hq, hkv, 128, 16, sizes,
+                              prefix, (0, 20), True, poison=True)
+    check(w, rows=sample_rows(w, per_seq_heads=1, seed=5))
+
+
+def test_shared_pools_past_4gib():
+    """The shared-prefix step on pools whose used blocks all lie past 4.25 GiB
+    equals, bit for bit, the same step on a small pool holding the same data."""
+    import paged_kv_cache_310_amd as pa
+    from test_gpu_large_pool import assert_lower_untouched, assert_same, lift, shift_blocks, \
+        shift_slots
+    # Tails of 0..2 tokens: some members copy their group's partial block in
+    # this step, others already have.
+    w = wl.make_shared_groups("shared_big", 4701, wl.BF16, 16, 2, 128, 16, [5, 1, 3],
+                              [700, 90, 2000], (0, 2), True, poison=True)
+    assert w.block_mapping is not None
+    ks, vs = to_dev(w.k_cache), to_dev(w.v_cache)
+    base, kb, vb = lift(ks, vs)
+    say("shared large pool: base block", base)
+    q, kn, vn, lens = to_dev(w.q), to_dev(w.k_new), to_dev(w.v_new), to_dev(w.context_lens)
+    gs, pl = to_dev(w.group_start), to_dev(w.prefix_lens)
+    outs = {}
+    for name, k, v, tab, slots, pairs in (
+            ("small", ks, vs, w.block_tables, w.slot_mapping, w.block_mapping),
+            ("large", kb, vb, shift_blocks(w.block_tables, base),
+             shift_slots(w.slot_mapping, base, 16), shift_blocks(w.block_mapping, base))):
+        pa.pa_copy_blocks(k, v, to_dev(pairs))
+        outs[name] = pa.pa_decode_shared(q, k, v, to_dev(tab), lens, float(w.scale), gs, pl,
+                                         k_new=kn, v_new=vn, slot_mapping=to_dev(slots))
+    torch.cuda.synchronize()
+    assert_same(outs["small"], outs["large"])
+    assert_same(ks, kb[base:])
+    assert_same(vs, vb[base:])
+    assert_lower_untouched(kb, base)
+    assert_lower_untouched(vb, base)
+    k_ref, v_ref = oracle_pools(w)
+    err = assert_attention_close(out_f64(outs["small"]), oracle_decode(w, k_ref, v_ref), wl.BF16)
+    say("max-abs %.3e row-rel %.3e" % err)
+    del kb, vb
+    torch.cuda.empty_cache()
 
 
 def test_shared_edge_cases():
