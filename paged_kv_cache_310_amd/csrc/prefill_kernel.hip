@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   __shared__ __attribute__((aligned(16))) char lds[kBufs][kBufBytes];
   __shared__ int32_t tab[kTableCap];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);   // wave-uniform: what derives from it stays scalar
   const int lane = tid & 63;
   const int g4 = lane >> 4;
   const int n = lane & 15;
@@ -418,13 +418,18 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
             for (int i = 0; i < 4; ++i)
               if (k0 + 16 * half + 4 * g4 + i > pos[rt]) x[4 * half + i] = -INFINITY;
         }
-        float mx = smax(smax(smax(x[0], x[1]), smax(x[2], x[3])),
-                        smax(smax(x[4], x[5]), smax(x[6], x[7])));
-        mx = group4_smax(mx);
-        // Tile max in the exp2 domain (cexp >= 0 keeps the order).
-        mx = mx == -INFINITY ? -INFINITY : mx * cexp;
-        const bool grow = mx > m_run[rt] + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mx_lane = smax(smax(smax(x[0], x[1]), smax(x[2], x[3])),
+                                   smax(smax(x[4], x[5]), smax(x[6], x[7])));
+        // A row's reference moves only if its tile max (the max over its four
+        // lanes) passes it by the slack, i.e. only if one of its lanes' own
+        // max does: the four-lane max is taken only in a step where some
+        // lane's does (in the exp2 domain; cexp >= 0 keeps the order).
+        const bool lane_grow =
+            (mx_lane == -INFINITY ? -INFINITY : mx_lane * cexp) > m_run[rt] + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(lane_grow)) {
+          float mx = group4_smax(mx_lane);
+          mx = mx == -INFINITY ? -INFINITY : mx * cexp;
+          const bool grow = mx > m_run[rt] + kRescaleSlack;
           const float m_new = grow ? mx : m_run[rt];
           // 1 where the reference stays (also for a row still at m = -inf,
           // where the difference would be NaN).
