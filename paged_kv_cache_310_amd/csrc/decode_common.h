@@ -193,12 +193,6 @@ __device__ __forceinline__ int64_t uniform(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ int64_t wave_sum(int64_t x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
-
 __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t x, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -223,6 +217,36 @@ __device__ __forceinline__ int wave_inclusive_scan32(int x) {
   x += dpp_or_zero<0x118, 0xf>(x);   // row_shr:8
   x += dpp_or_zero<0x142, 0xa>(x);   // row_bcast:15
   x += dpp_or_zero<0x143, 0xc>(x);   // row_bcast:31
+  return x;
+}
+
+// Lane `src`'s x (src wave-uniform), read with v_readlane: no LDS-crossbar
+// round trip, unlike a shuffle.
+__device__ __forceinline__ int lane_value(int x, int src) {
+  return __builtin_amdgcn_readlane(x, src);
+}
+__device__ __forceinline__ int64_t lane_value(int64_t x, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)x, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), src);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Inclusive prefix sum over the 64 lanes: the DPP scan when every value lies
+// in [0, 2^24) (the total then stays below 2^31), else the shuffle scan.
+__device__ __forceinline__ int64_t wave_scan(int64_t x, int lane) {
+  if (__ballot(x < 0 || x >= (1 << 24)) == 0) return wave_inclusive_scan32((int)x);
+  return wave_inclusive_scan(x, lane);
+}
+
+// Sum over the 64 lanes, on every lane.  When every value lies in [0, 2^24)
+// the total stays below 2^31: one DPP scan and a lane read, where the
+// shuffle butterfly costs six dependent LDS-crossbar round trips per 32-bit
+// half (about 1 us of a short launch's start-up).
+__device__ __forceinline__ int64_t wave_sum(int64_t x) {
+  if (__ballot(x < 0 || x >= (1 << 24)) == 0)
+    return lane_value(wave_inclusive_scan32((int)x), 63);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
   return x;
 }
 
@@ -297,14 +321,14 @@ __device__ void locate_units(const SplitLds& C, const int32_t* lens, int num_seq
     } else {
       incl = wave_inclusive_scan((int64_t)un, lane);
     }
-    const int64_t tot = uniform((int64_t)__shfl(incl, 63));
+    const int64_t tot = lane_value(incl, 63);
     auto probe = [&](int64_t r, UnitHit& hit) {
       if (hit.found || r >= acc_u + tot) return;
       const unsigned long long above = __ballot(acc_u + incl > r);
       const int first = __ffsll((long long)above) - 1;
       hit.found = true;
       hit.s = uniform(base + first);
-      hit.bu = uniform((int64_t)(acc_u + __shfl(incl - un, first)));
+      hit.bu = acc_u + lane_value((int64_t)(incl - un), first);
       const int64_t ne_before = acc_ne + __popcll(ne & ((1ull << first) - 1));
       hit.bc = hit.bu - (int64_t)seg_cost * ne_before;
       hit.off = r - hit.bu;
@@ -536,14 +560,14 @@ __device__ void tail_locate_units(const SplitLds& C, const int32_t* lens,
     } else {
       incl = wave_inclusive_scan((int64_t)un, lane);
     }
-    const int64_t tot = uniform((int64_t)__shfl(incl, 63));
+    const int64_t tot = lane_value(incl, 63);
     auto probe = [&](int64_t r, UnitHit& hit) {
       if (hit.found || r >= acc_u + tot) return;
       const unsigned long long above = __ballot(acc_u + incl > r);
       const int first = __ffsll((long long)above) - 1;
       hit.found = true;
       hit.s = uniform(base + first);
-      hit.bu = uniform((int64_t)(acc_u + __shfl(incl - un, first)));
+      hit.bu = acc_u + lane_value((int64_t)(incl - un), first);
       const int64_t ne_before = acc_ne + __popcll(ne & ((1ull << first) - 1));
       hit.bc = hit.bu - (int64_t)seg_cost * ne_before;
       hit.off = r - hit.bu;

@@ -123,22 +123,22 @@ __device__ void prefix_locate(const ShareArgs& sh, const int32_t* lens, int B, i
     if (g < sh.num_groups) pg = prefix_group_lane(sh, lens, B, g);
     const int64_t un = (int64_t)pg.nb * (pg.c0 + seg_cost);
     const int64_t cn = (int64_t)pg.nb * pg.c0;
-    const int64_t incl_u = wave_inclusive_scan(un, lane);
-    const int64_t incl_c = wave_inclusive_scan(cn, lane);
-    const int64_t tot_u = uniform((int64_t)__shfl(incl_u, 63));
-    const int64_t tot_c = uniform((int64_t)__shfl(incl_c, 63));
+    const int64_t incl_u = wave_scan(un, lane);
+    const int64_t incl_c = wave_scan(cn, lane);
+    const int64_t tot_u = lane_value((int64_t)incl_u, 63);
+    const int64_t tot_c = lane_value((int64_t)incl_c, 63);
     auto probe = [&](int64_t r, PHit& hit) {
       if (hit.found || r >= acc_u + tot_u) return;
       const int first = __ffsll((long long)__ballot(acc_u + incl_u > r)) - 1;
       hit.found = true;
       hit.g = uniform(base + first);
-      hit.bu = uniform((int64_t)(acc_u + __shfl(incl_u - un, first)));
-      hit.bc = uniform((int64_t)(acc_c + __shfl(incl_c - cn, first)));
+      hit.bu = acc_u + lane_value((int64_t)(incl_u - un), first);
+      hit.bc = acc_c + lane_value((int64_t)(incl_c - cn), first);
       hit.off = r - hit.bu;
-      hit.pg.lo = uniform(__shfl(pg.lo, first));
-      hit.pg.nmem = uniform(__shfl(pg.nmem, first));
-      hit.pg.c0 = uniform(__shfl(pg.c0, first));
-      hit.pg.nb = uniform(__shfl(pg.nb, first));
+      hit.pg.lo = lane_value(pg.lo, first);
+      hit.pg.nmem = lane_value(pg.nmem, first);
+      hit.pg.c0 = lane_value(pg.c0, first);
+      hit.pg.nb = lane_value(pg.nb, first);
     };
     probe(r0, h0);
     probe(r1, h1);
