@@ -342,17 +342,30 @@ __device__ void locate_units(const SplitLds& C, const int32_t* lens, int num_seq
 
 // Computes the split for worker w; false when w has no chunks.  Caches the
 // sequences' lengths in C on the way.
+// Lane's values v[k] = a[base + 64 k + lane], k < 4 (0 past a[n - 1]): four
+// range-checked loads issued together, one memory latency for 256 entries.
+__device__ __forceinline__ void load_block256(const int32_t* a, int n, int base, int lane,
+                                              int v[4]) {
+  const int left = n - base;
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(a + base, (left < 256 ? left : 256) * 4);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    v[k] = (int)__builtin_amdgcn_raw_buffer_load_b32(r, (k * 64 + lane) * 4, 0, 0);
+}
+
 __device__ __forceinline__ bool split_line(SplitLds& C, const int32_t* lens, int num_seqs,
                                            int num_heads, int seg_cost, int nworkers, int w,
                                            int lane, LineSplit& ls) {
   int64_t wseq = 0, useq = 0;
   for (int base = 0; base < num_seqs; base += 256) {
     int64_t n = 0, un = 0;
+    int Lb[4];
+    load_block256(lens, num_seqs, base, lane, Lb);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int sq = base + k * 64 + lane;
       if (sq < num_seqs) {
-        const int L = lens[sq];
+        const int L = Lb[k];
         if (sq < kLenCache) ((lds_i32*)C.len)[sq] = L;
         const int c = chunks_of(L);
         n += c;
@@ -519,12 +532,15 @@ __device__ __forceinline__ void tail_line_totals(SplitLds& C, const int32_t* len
   useq = 0;
   for (int base = 0; base < num_seqs; base += 256) {
     int64_t n = 0, un = 0;
+    int Lb[4], Pb[4];
+    load_block256(lens, num_seqs, base, lane, Lb);
+    load_block256(prefix_lens, num_seqs, base, lane, Pb);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int sq = base + k * 64 + lane;
       if (sq < num_seqs) {
-        const int L = lens[sq];
-        const int c = chunks_of(L) - shared_chunks(L, prefix_lens[sq]);
+        const int L = Lb[k];
+        const int c = chunks_of(L) - shared_chunks(L, Pb[k]);
         if (sq < kLenCache) ((lds_i32*)C.len)[sq] = c;
         n += c;
         un += c > 0 ? c + seg_cost : 0;
