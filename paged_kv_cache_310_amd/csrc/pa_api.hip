@@ -152,7 +152,7 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
   if (pa::decode_resident_per_cu(dtype, head_dim, block_size, group, &resident) != hipSuccess ||
       resident <= 0)
     return PA_ERR_HIP;
-  *out = cus * (resident < pa::kWavesPerCu ? resident : pa::kWavesPerCu);
+  *out = cus * (resident < pa::kDecodeWavesPerCu ? resident : pa::kDecodeWavesPerCu);
   return PA_OK;
 }
 
@@ -166,8 +166,8 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
 // table width, an upper bound of every context, so P = one piece per 8
 // 16-token chunks of that width, clamped to [16, 48].  Tables of 1,024
 // chunks (16k tokens) or more take 64 pieces while that stays within half
-// the resident workers: one sequence at 16k-64k then gains 5-14% of its
-// step.  At 8k, or with the device already full (two sequences at 16k or
+// of CUs x kWavesPerCu workers: one sequence at 16k-64k then gains 5-14% of
+// its step.  At 8k, or with the device already full (two sequences at 16k or
 // 32k), the extra pieces cost more merge time than they save.
 constexpr int64_t kChunksPerPiece = 8;
 constexpr int64_t kMinPiecesPerSegment = 16;
@@ -186,7 +186,10 @@ int default_workers_for_call(int dtype, int head_dim, int block_size, int max_bl
   int64_t pieces = chunks / kChunksPerPiece;
   pieces = pieces < kMinPiecesPerSegment ? kMinPiecesPerSegment : pieces;
   pieces = pieces > kMaxPiecesPerSegment ? kMaxPiecesPerSegment : pieces;
-  if (chunks >= kLongTableChunks && kLongTablePieces * segments * 2 <= workers)
+  int bound = 0;
+  const int sb = default_workers_for_current_device(&bound);
+  if (sb != PA_OK) return sb;
+  if (chunks >= kLongTableChunks && kLongTablePieces * segments * 2 <= bound)
     pieces = kLongTablePieces;
   int64_t cap = pieces * segments;
   cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;

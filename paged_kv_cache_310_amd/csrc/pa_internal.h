@@ -195,11 +195,19 @@ hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const 
 hipError_t launch_copy(void* k_cache, void* v_cache, const int64_t* block_mapping,
                        int64_t num_pairs, int64_t block_bytes, hipStream_t stream);
 
-// Default decode workers per CU (one wave per SIMD).  Measured on the
-// long-context and OPT-shaped batches, 2..16 workers per CU are within 4% of
-// each other (fewer is slightly better: fewer split segments and fewer
-// concurrent streams), while batches that share prefix blocks gain ~25% from
-// 4 over 2, because sharers then run at the same time on one XCD's L2.
+// Workers per CU of the shared-prefix decode, and the upper bound of every
+// default worker count (what pa_decode_default_workers reports for sizing a
+// workspace).  The shared-prefix kernel loses 8% at 3 per CU: its prefix row
+// blocks and the tails of the same sequences meet in an XCD's L2 only while
+// enough workers run at once.
 constexpr int kWavesPerCu = 4;
+// Workers per CU of pa_decode.  Measured interleaved against 4: 1.1% faster
+// on the long-context batch, 1.9% on the OPT-shaped one, 0.4-0.9% on the
+// grouped-query Pareto batches and 3% on mid-size batches (fewer split
+// segments to merge, fewer concurrent tile streams).  Plain decode of a batch
+// whose sequences share prefix blocks was 9.5% slower at 3 (sharers re-read
+// the prefix through L2 only while enough workers run at once); such batches
+// are what pa_decode_shared is for.
+constexpr int kDecodeWavesPerCu = 3;
 
 }  // namespace pa
