@@ -15,13 +15,12 @@
 // pair of the KV head's group, token-major, so grouped query heads share
 // every K/V tile.  Each wave owns 32 rows as two 16-row MFMA tiles,
 // interleaved with the other waves' tiles.  The workgroup walks the keys in
-// steps of 32 (two 16-token halves): all threads load a step's K and V rows
-// through the table into registers kDepth steps ahead and store them to one
-// of kDepth + 1 LDS buffers after the step before it is computed, so the
-// global loads of the next steps overlap the products of this one and one
-// barrier per step suffices.  The sequence's block-table entries are staged
-// in LDS (kTableCap at a time), so no step waits on a table read before it
-// can address its K/V rows.
+// steps of 32 (two 16-token halves).  A step's K and V rows go from the pool
+// straight into one of two LDS buffers (buffer loads with an LDS destination,
+// no trip through registers), issued one step ahead, so they arrive while the
+// step before is computed; one barrier per step publishes them.  The
+// sequence's block-table entries are staged in LDS (kTableCap at a time), so
+// no step waits on a table read before it can address its K/V rows.
 //
 // Per step and 16-row tile (lane l, lane group g = l/16, column n = l%16):
 //  * S^T[16 keys x 16 rows] = K . Q^T for each 16-key half, four
@@ -62,19 +61,23 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowTiles = 2;                  // 16-row MFMA tiles per wave
 constexpr int kRowsPerWave = 16 * kRowTiles;
 static_assert(kWaves * kRowsPerWave == kPrefillRowsPerWg, "rows per workgroup");
-// K rows are padded by 16 bytes in LDS: the 16 rows one A-operand read
-// touches then start on 16 different 4-bank groups.
-constexpr int kKStride = kPRow + 16;
-constexpr int kKBytes = kKeys * kKStride;
-// V rows are padded by 32 bytes: the 16 rows one transposing read touches
-// (32 bytes each) then fill the 64 banks exactly twice.
-constexpr int kVStride = kPRow + 32;
-constexpr int kVBytes = kKeys * kVStride;
+// A step's K and V tiles in LDS, 32 keys x 256 bytes each, unpadded: the
+// loads that fill them write 1 KiB runs (lane i of a load writes bytes
+// 16 i..16 i + 15 of its run), so the layout is chosen by which pool chunk
+// each lane fetches.  With r a key of the step and ch a 16-byte chunk of its
+// row (dims 8 ch..8 ch + 7):
+//  * K chunk (r, ch) sits at (r / 16) 4096 + 256 ch + 16 (r % 16): a 256-byte
+//    line per chunk index and 16-key half, one slot per key;
+//  * V chunk (r, ch) sits at (r / 16) 4096 + 256 (2 (ch / 2) + (r % 16) / 8)
+//    + 16 (2 (r % 8) + ch % 2): a line per chunk pair and 8 keys.
+// The A-operand reads of K (16 keys, one chunk index per 16 lanes) and the
+// transposing reads of V (16 keys x two chunks per 32 lanes) then touch each
+// of the 64 banks at most once per cycle, and every read address is a
+// per-lane constant plus an immediate.
+constexpr int kKBytes = kKeys * kPRow;
+constexpr int kVBytes = kKeys * kPRow;
 constexpr int kBufBytes = kKBytes + kVBytes;
-// Steps whose K/V loads are in flight ahead of the step being computed; the
-// workgroup holds kDepth + 1 LDS buffers.
-constexpr int kDepth = 1;
-constexpr int kBufs = kDepth + 1;
+constexpr int kHalfBytes = kBufBytes / 4;   // one 16-key half of the K (or V) tile
 // Block-table entries held in LDS at a time (refilled every
 // kTableCap * BS / kKeys steps).
 constexpr int kTableCap = 1024;
@@ -91,8 +94,13 @@ typedef uint32_t __attribute__((address_space(3))) lds_u32;
 __device__ __forceinline__ u32x4 lds_load16(const char* base, int offset) {
   return *reinterpret_cast<const u32x4*>(base + offset);
 }
-__device__ __forceinline__ void lds_store16(char* base, int offset, const u32x4& v) {
-  *reinterpret_cast<u32x4*>(base + offset) = v;
+typedef __attribute__((address_space(3))) void lds_void;
+// One 16-byte pool chunk per lane into LDS: lane i's chunk (at `offset` +
+// `soffset` in the range of r, or 0 outside it) lands at dst + 16 i.  dst is
+// wave-uniform.
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, char* dst, int offset,
+                                            int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, offset, soffset, 0, 0);
 }
 
 typedef short i16x4_t_lds __attribute__((ext_vector_type(4)));
@@ -146,7 +154,12 @@ template <int BS, bool kSplit>
 // costs a few spilled registers and measured faster than two workgroups.
 __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs a,
                                                                const SplitArgs sp) {
-  __shared__ __attribute__((aligned(16))) char lds[kBufs][kBufBytes];
+  // Two step buffers as two LDS objects, each accessed by name in the
+  // (two-fold unrolled) step loop: the compiler can then tell a buffer's
+  // reads from the other buffer's in-flight loads, and does not wait for
+  // those loads before reading.
+  __shared__ __attribute__((aligned(16))) char lds0[kBufBytes];
+  __shared__ __attribute__((aligned(16))) char lds1[kBufBytes];
   __shared__ int32_t tab[kTableCap];
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);   // wave-uniform: what derives from it stays scalar
@@ -266,45 +279,47 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   if (!kSplit || t_begin < t_end) stage_table(t_begin / kStepsPerTable * kTableCap);
   __syncthreads();
 
-  // Step loads: thread tid moves key tid/16 + (kThreads/16) h of the step,
-  // 16 bytes (dims 8*(tid%16)..+8), for h < kLoads; keys at or past L load
-  // zeros.
+  // Step loads.  Wave w fills lines 4 (2 (w % 2) + h) .. + 3 of half w / 2
+  // of both tiles (h = 0, 1): a half's 16 keys lie in one block (BS is a
+  // multiple of 16 and a step starts at a multiple of 32), so the block, its
+  // table entry and its buffer range are wave-uniform.  The range holds the
+  // block's rows below L: rows past it (or a block past the context) load as
+  // zeros.  Lane i of load h fetches, for K, chunk 4 (2 (w % 2) + h) + i / 16
+  // of the half's key i % 16; for V, chunk 4 (2 (w % 2) + h) + 2 (i / 32)
+  // + i % 2 of key 8 ((i / 16) % 2) + (i % 16) / 2: the layouts above.  Its
+  // offset in the range is fixed but for h (64 bytes apart).
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
-  constexpr int kKeysPerPass = kThreads / 16;
-  constexpr int kLoads = kKeys / kKeysPerPass;
-  const int key_in_step = tid >> 4;
-  const int chunk = (tid & 15) * 16;
-  u32x4 kr[kDepth][kLoads], vr[kDepth][kLoads];
-  // Load h of a step covers the 16 keys k0 + 16 h .. +16, all in one block
-  // (BS is a multiple of 16 and k0 of kKeys), so the block, its table entry
-  // and its buffer range are wave-uniform: the range holds the block's rows
-  // below L, and rows past it (or a block past the context) read as zeros
-  // without a branch.  A lane's offset in the range is fixed per h.
+  const int fetch_half = wave >> 1;
+  const int fetch_run = 2 * (wave & 1);           // first of the wave's two 1 KiB runs in the half
+  const int kkey = (16 * fetch_half + (lane & 15)) % BS;
+  const int vkey = (16 * fetch_half + 8 * ((lane >> 4) & 1) + ((lane & 15) >> 1)) % BS;
+  const int koff = kkey * kPRow + 64 * fetch_run + 16 * (lane >> 4);
+  const int voff = vkey * kPRow + 64 * fetch_run + 32 * (lane >> 5) + 16 * (lane & 1);
   const int64_t block_bytes = (int64_t)HKV * BS * kPRow;
   const int64_t head_bytes = (int64_t)hk * BS * kPRow;
-  auto fetch = [&](int k0, int slot) {
+  auto fetch = [&](int k0, char* buf) {
+    const int bi = (k0 + 16 * fetch_half) / BS;   // non-negative: shifts only
+    const int rows_valid = uniform(min(max(L - bi * BS, 0), BS));
+    const int64_t pb = rows_valid > 0 ? (int64_t)uniform(tab[bi % kTableCap]) : 0;
+    const int64_t base = pb * block_bytes + head_bytes;
+    const int bytes = rows_valid * kPRow;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + base, bytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + base, bytes);
+    char* kdst = buf + fetch_half * kHalfBytes + fetch_run * 1024;
+    char* vdst = kdst + kKBytes;
 #pragma unroll
-    for (int h = 0; h < kLoads; ++h) {
-      const int kg = k0 + kKeysPerPass * h;   // first key of the 16
-      const int bi = kg / BS;                 // non-negative: shifts only
-      const int rows_valid = uniform(min(max(L - bi * BS, 0), BS));
-      const int64_t pb = rows_valid > 0 ? (int64_t)uniform(tab[bi % kTableCap]) : 0;
-      const int64_t base = pb * block_bytes + head_bytes;
-      const int bytes = rows_valid * kPRow;
-      const int loff = ((kg % BS) + key_in_step) * kPRow + chunk;
-      kr[slot][h] = load16(tile_rsrc(kc + base, bytes), loff);
-      vr[slot][h] = load16(tile_rsrc(vc + base, bytes), loff);
+    for (int h = 0; h < 2; ++h) {
+      load_to_lds(rk, kdst + 1024 * h, koff, 64 * h);
+      load_to_lds(rv, vdst + 1024 * h, voff, 64 * h);
     }
   };
-  auto stash = [&](int slot, int buf) {
-#pragma unroll
-    for (int h = 0; h < kLoads; ++h) {
-      const int key = key_in_step + kKeysPerPass * h;
-      lds_store16(lds[buf], key * kKStride + chunk, kr[slot][h]);
-      lds_store16(lds[buf] + kKBytes, key * kVStride + chunk, vr[slot][h]);
-    }
-  };
+  // Where this lane's operand reads start in a buffer's K and V tiles (the
+  // layouts above): K chunk 4c + g4 of key 16 half + n at kread + 1024 c
+  // + 4096 half; V chunk 2c + (n % 4) / 2 of key 4 g4 + n / 4 at vread
+  // + 512 c, byte 8 (n % 2) of it (keys 16.. 4096 bytes on).
+  const int kread = 256 * g4 + 16 * n;
+  const int vread = 256 * (g4 >> 1) + 16 * (8 * (g4 & 1) + 2 * (n >> 2) + ((n >> 1) & 1)) + 8 * (n & 1);
 
   f32x4_t acc[kRowTiles][8];
   float m_run[kRowTiles], l_run[kRowTiles];
@@ -316,34 +331,16 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
     for (int c = 0; c < 8; ++c) acc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Step j's rows travel in register slot j % kDepth and LDS buffer
-  // j % kBufs.  The slot is free again once step j is stashed, the buffer
-  // once step j is computed (kBufs - 1 iterations before it is refilled).
-  if constexpr (kSplit) {
-    // A split may start anywhere in a table window, so the first kDepth
-    // steps can reach into the next one: restage it there, as the loop does.
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-      const int tj = t_begin + j;
-      if (tj >= t_end) break;
-      if (j > 0 && tj % kStepsPerTable == 0) {
-        __syncthreads();
-        stage_table(tj / kStepsPerTable * kTableCap);
-        __syncthreads();
-      }
-      fetch(tj * kKeys, tj % kDepth);
-    }
-    if (t_begin < t_end) stash(t_begin % kDepth, t_begin % kBufs);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j)
-      if (j < steps) fetch(j * kKeys, j);
-    stash(0, 0);
-  }
+  // Step t_begin + 2i goes to LDS buffer lds0, step t_begin + 2i + 1 to
+  // lds1, each loaded during the step before it: the buffer held the step
+  // two back, which every wave finished before the barrier that closed the
+  // step before.  That barrier also waits for the loads (a barrier waits for
+  // the wave's outstanding memory operations).
+  if (t_begin < t_end) fetch(t_begin * kKeys, lds0);
   __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
+  auto step = [&](const char* kb, char* next, int t) __attribute__((always_inline)) {
     const int k0 = t * kKeys;
-    const int ahead = t + kDepth;
+    const int ahead = t + 1;
     if (ahead < t_end) {
       if (ahead % kStepsPerTable == 0) {
         // Step `ahead` needs the next table window; every fetch of the
@@ -352,23 +349,22 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
         stage_table(ahead / kStepsPerTable * kTableCap);
         __syncthreads();
       }
-      fetch(ahead * kKeys, t % kDepth);
+      fetch(ahead * kKeys, next);
     }
     if (wave_rows && k0 <= wave_pmax) {
       // Some key of the step lies past some row's position (this includes
       // every key at or past L).
       const bool diagonal = k0 + kKeys - 1 > wave_pmin;
-      const char* kb = lds[t % kBufs];
       const char* vb = kb + kKBytes;
       // V^T operand of dim tile c (dims 16c..16c+15): lane n of group g
       // needs V[key][16c + n] for its eight keys (k = 8g..8g+7: keys
       // 4g..4g+3, then 16+4g..16+4g+3).  In each of two transposing reads,
       // lane n of the group addresses key 4g + n/4 (+16), dims 16c + 4(n%4)
-      // ..+4, and receives V[4g + e (+16)][16c + n], e = 0..3.
+      // ..+4 (chunk 2c + (n%4)/2, its half n%2), and receives
+      // V[4g + e (+16)][16c + n], e = 0..3.
       auto v_operand = [&](int c) {
-        const int col = (16 * c + 4 * (n & 3)) * 2;
-        const uint64_t lo = lds_read_tr16(vb, (4 * g4 + (n >> 2)) * kVStride + col);
-        const uint64_t hi = lds_read_tr16(vb, (16 + 4 * g4 + (n >> 2)) * kVStride + col);
+        const uint64_t lo = lds_read_tr16(vb, vread + 512 * c);
+        const uint64_t hi = lds_read_tr16(vb, vread + 512 * c + kHalfBytes);
         return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
       };
       // Scores of both row tiles first, the four independent accumulators
@@ -380,11 +376,11 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
         for (int half = 0; half < 2; ++half) scores[rt][half] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        // K operands of dims 32c + 8g..+8: key 16*half + n.
+        // K operands of dims 32c + 8g..+8 (chunk 4c + g): key 16*half + n.
         u32x4 kop[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half)
-          kop[half] = lds_load16(kb, (16 * half + n) * kKStride + c * 64 + g4 * 16);
+          kop[half] = lds_load16(kb, kread + 1024 * c + kHalfBytes * half);
 #pragma unroll
         for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
@@ -473,8 +469,11 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
               acc[rt][c], 0, 0, 0);
       }
     }
-    if (t + 1 < t_end) stash((t + 1) % kDepth, (t + 1) % kBufs);
     __syncthreads();
+  };
+  for (int t = t_begin; t < t_end; t += 2) {
+    step(lds0, lds1, t);
+    if (t + 1 < t_end) step(lds1, lds0, t + 1);
   }
 
   if constexpr (kSplit) {
