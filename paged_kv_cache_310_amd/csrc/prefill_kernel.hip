@@ -84,9 +84,10 @@ constexpr int kTableCap = 1024;
 // log2 of the largest weight the lazy rescale lets through.
 constexpr float kRescaleSlack = 8.f;
 // Dim tiles whose V^T operand is read ahead of its P.V products: the first
-// one's LDS reads are issued before the softmax, and each product's operand
-// one tile before it is used.  One tile ahead is 4-5% faster than none; two
-// or four spill registers at three workgroups per CU and are slower.
+// ones' LDS reads are issued before the softmax, and each product's operand
+// that many tiles before it is used.  One tile ahead is 4-5% faster than
+// none; two (166 registers, no spills) measured from 2.5% faster to 1.5%
+// slower on different boxes; four spill at three workgroups per CU.
 constexpr int kVAhead = 1;
 
 typedef uint32_t __attribute__((address_space(3))) lds_u32;
@@ -183,11 +184,20 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   // takes the same decision from the batch: causal work (n^2 / 2 per
   // sequence) against work on the earlier context (n (L - n)).
   // (Each wave sums over all sequences itself, so no barrier is needed.)
+  // Lane q < 64 keeps sequence q's chunk start, end and length, so that a
+  // batch of up to 64 sequences needs no second round trip for its own.
   float causal_all = 0.f, earlier_all = 0.f;
+  int own_q0 = 0, own_q1 = 0, own_len = 0;
   for (int q = lane; q < a.num_seqs; q += 64) {
-    const float nq_s = (float)(a.query_start[q + 1] - a.query_start[q]);
+    const int qs = a.query_start[q], qe = a.query_start[q + 1], lq = a.context_lens[q];
+    if (q == lane) {
+      own_q0 = qs;
+      own_q1 = qe;
+      own_len = lq;
+    }
+    const float nq_s = (float)(qe - qs);
     causal_all += 0.5f * nq_s * nq_s;
-    earlier_all += nq_s * ((float)a.context_lens[q] - nq_s);
+    earlier_all += nq_s * ((float)lq - nq_s);
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
@@ -215,9 +225,10 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   if (pair >= pairs) return;
   const int s = pair / HKV;
   const int hk = pair % HKV;
-  const int q0 = a.query_start[s];
-  const int nq = a.query_start[s + 1] - q0;
-  const int L = a.context_lens[s];
+  const bool own = a.num_seqs <= 64;
+  const int q0 = own ? __builtin_amdgcn_readlane(own_q0, s) : a.query_start[s];
+  const int nq = (own ? __builtin_amdgcn_readlane(own_q1, s) : a.query_start[s + 1]) - q0;
+  const int L = own ? __builtin_amdgcn_readlane(own_len, s) : a.context_lens[s];
   const int rows = nq * G;
   const int row0 = tile * kPrefillRowsPerWg;
   if (row0 >= rows) return;                       // the whole workgroup leaves
@@ -276,8 +287,6 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
       tab[i] = table[first + i];
   };
   constexpr int kStepsPerTable = kTableCap * BS / kKeys;
-  if (!kSplit || t_begin < t_end) stage_table(t_begin / kStepsPerTable * kTableCap);
-  __syncthreads();
 
   // Step loads.  Wave w fills lines 4 (2 (w % 2) + h) .. + 3 of half w / 2
   // of both tiles (h = 0, 1): a half's 16 keys lie in one block (BS is a
@@ -298,10 +307,13 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   const int voff = vkey * kPRow + 64 * fetch_run + 32 * (lane >> 5) + 16 * (lane & 1);
   const int64_t block_bytes = (int64_t)HKV * BS * kPRow;
   const int64_t head_bytes = (int64_t)hk * BS * kPRow;
-  auto fetch = [&](int k0, char* buf) {
+  // direct: the block's table entry is read from the table itself (the
+  // first step, issued while the window is being staged).
+  auto fetch = [&](int k0, char* buf, bool direct) {
     const int bi = (k0 + 16 * fetch_half) / BS;   // non-negative: shifts only
     const int rows_valid = uniform(min(max(L - bi * BS, 0), BS));
-    const int64_t pb = rows_valid > 0 ? (int64_t)uniform(tab[bi % kTableCap]) : 0;
+    const int64_t pb =
+        rows_valid > 0 ? (int64_t)uniform(direct ? table[bi] : tab[bi % kTableCap]) : 0;
     const int64_t base = pb * block_bytes + head_bytes;
     const int bytes = rows_valid * kPRow;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + base, bytes);
@@ -336,7 +348,8 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   // two back, which every wave finished before the barrier that closed the
   // step before.  That barrier also waits for the loads (a barrier waits for
   // the wave's outstanding memory operations).
-  if (t_begin < t_end) fetch(t_begin * kKeys, lds0);
+  if (!kSplit || t_begin < t_end) stage_table(t_begin / kStepsPerTable * kTableCap);
+  if (t_begin < t_end) fetch(t_begin * kKeys, lds0, true);
   __syncthreads();
   auto step = [&](const char* kb, char* next, int t) __attribute__((always_inline)) {
     const int k0 = t * kKeys;
@@ -349,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
         stage_table(ahead / kStepsPerTable * kTableCap);
         __syncthreads();
       }
-      fetch(ahead * kKeys, next);
+      fetch(ahead * kKeys, next, false);
     }
     if (wave_rows && k0 <= wave_pmax) {
       // Some key of the step lies past some row's position (this includes

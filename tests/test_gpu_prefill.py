@@ -64,6 +64,22 @@ def test_small_ragged(hq, hkv, bs):
     say("max-abs %.3e row-rel %.3e" % err)
 
 
+@pytest.mark.parametrize("nseq", [64, 65, 130])
+def test_many_sequences(nseq):
+    """Batches of up to 64 sequences take each sequence's chunk bounds from
+    the lanes that summed the batch; larger ones read them again: both sides
+    of that edge, ragged fresh prompts and chunks."""
+    say("prefill many sequences", nseq)
+    rng = np.random.default_rng(700 + nseq)
+    ctx = [int(x) for x in rng.integers(1, 90, nseq)]
+    nq = [int(rng.integers(0, c + 1)) if i % 3 else c for i, c in enumerate(ctx)]
+    w = wl.make_prefill("many", 710 + nseq, wl.BF16, 8, 2, 128, 16, ctx, nq)
+    got = out_f64(run_device(w))
+    ref = oracle_rows(w)
+    err = assert_attention_close(got, ref, wl.BF16)
+    say("max-abs %.3e row-rel %.3e" % err)
+
+
 @pytest.mark.parametrize("bs", [16, 32])
 def test_long_context_crosses_table_windows(bs):
     """Contexts past 1024 table entries: the kernel restages its LDS copy of
