@@ -13,8 +13,8 @@
 // (sequence, KV head) pair, the pairs dealt to the XCDs so that a pair's
 // workgroups share its K/V in one L2.  A row is a (query token, query head)
 // pair of the KV head's group, token-major, so grouped query heads share
-// every K/V tile.  Each wave owns 32 rows as two 16-row MFMA tiles,
-// interleaved with the other waves' tiles.  The workgroup walks the keys in
+// every K/V tile.  Each wave owns 32 consecutive rows as two 16-row MFMA
+// tiles.  The workgroup walks the keys in
 // steps of 32 (two 16-token halves).  A step's K and V rows go from the pool
 // straight into one of two LDS buffers (buffer loads with an LDS destination,
 // no trip through registers), issued one step ahead, so they arrive while the
@@ -240,10 +240,13 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   const int t_begin = kSplit ? min(steps, split * split_steps) : 0;
   const int t_end = kSplit ? min(steps, t_begin + split_steps) : steps;
 
-  // Row tile rt of wave w covers rows row0 + 16 (rt kWaves + w) .. +16: the
-  // waves' tiles interleave, so under the causal mask the waves of a
-  // workgroup see nearly the same number of keys.
-  auto tile_row0 = [&](int rt) { return row0 + 16 * (rt * kWaves + wave); };
+  // Row tile rt of wave w covers rows row0 + 16 (w kRowTiles + rt) .. +16:
+  // a wave's two tiles are adjacent, so under the causal mask its lower tile
+  // computes at most one step of keys none of its rows sees (interleaving the
+  // waves' tiles instead evens out the waves' key counts but makes the lower
+  // tile of every wave compute two such steps: 16% more matrix work on fresh
+  // prompts against 5%, and 1.5-2% slower).
+  auto tile_row0 = [&](int rt) { return row0 + 16 * (wave * kRowTiles + rt); };
   const bool wave_rows = tile_row0(0) < rows;
   int wave_last = -1;                              // last real row of this wave
 #pragma unroll
