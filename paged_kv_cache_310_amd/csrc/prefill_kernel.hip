@@ -338,9 +338,16 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
 
   f32x4_t acc[kRowTiles][8];
   float m_run[kRowTiles], l_run[kRowTiles];
+  // The lazy-rescale bound in raw score units, (m + kRescaleSlack) / cexp:
+  // a lane whose raw maximum passes it may move its row's reference.  With
+  // cexp == 0 it is -inf until the first step (m = -inf) and +inf after it
+  // (m = 0), as the scaled test would be.
+  float raw_bound[kRowTiles];
+  const float inv_cexp = 1.f / cexp;
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
     m_run[rt] = -INFINITY;
+    raw_bound[rt] = -INFINITY;
     l_run[rt] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -436,8 +443,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
         // lanes) passes it by the slack, i.e. only if one of its lanes' own
         // max does: the four-lane max is taken only in a step where some
         // lane's does (in the exp2 domain; cexp >= 0 keeps the order).
-        const bool lane_grow =
-            (mx_lane == -INFINITY ? -INFINITY : mx_lane * cexp) > m_run[rt] + kRescaleSlack;
+        const bool lane_grow = mx_lane > raw_bound[rt];
         if (__builtin_amdgcn_ballot_w64(lane_grow)) {
           float mx = group4_smax(mx_lane);
           mx = mx == -INFINITY ? -INFINITY : mx * cexp;
@@ -448,6 +454,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
           const float alpha =
               !kSplit || grow ? fast_exp2(m_run[rt] - m_new) : 1.f;
           m_run[rt] = m_new;
+          raw_bound[rt] = (m_new + kRescaleSlack) * inv_cexp;
           l_run[rt] *= alpha;
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) acc[rt][cc] *= alpha;
