@@ -83,6 +83,26 @@ def test_splits_cross_table_windows(bs, splits):
     say("max-abs %.3e row-rel %.3e" % err)
 
 
+# (block size, context, splits) whose split of one query token starts one
+# step before, two steps before, or on the first step of a block-table window
+# (512 steps of 32 keys at 16-token blocks, 1,024 at 32): split 7 of 8 over
+# 580 steps starts at step 511, split 6 of 7 over 590 at 510, split 8 of 9
+# over 570 at 512, and split 3 of 4 over 1,362 at 1,023.
+WINDOW_EDGES = [(16, 18560, 8), (16, 18880, 7), (16, 18240, 9), (32, 43584, 4)]
+
+
+@pytest.mark.parametrize("bs,ctx,splits", WINDOW_EDGES)
+def test_split_starts_at_table_window_edges(bs, ctx, splits):
+    """A split's first step reads its table entries directly and later ones
+    through the staged window, restaged a step ahead of each boundary: a
+    split that starts just before, or on, a window boundary still reads every
+    block through the right window."""
+    say("prefill split window edge", bs, ctx, splits)
+    w = wl.make_prefill("splitedge", 760 + splits, wl.BF16, 4, 2, 128, bs, [ctx], [1])
+    err = assert_attention_close(out_f64(run_split(w, splits)), oracle_rows(w), wl.BF16)
+    say("max-abs %.3e row-rel %.3e" % err)
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0])
 def test_split_any_scale(scale):
     w = wl.make_prefill("splitscale", 730, wl.BF16, 8, 2, 128, 16, [70, 600, 2000],
