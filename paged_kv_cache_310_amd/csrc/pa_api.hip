@@ -152,7 +152,10 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
   if (pa::decode_resident_per_cu(dtype, head_dim, block_size, group, &resident) != hipSuccess ||
       resident <= 0)
     return PA_ERR_HIP;
-  *out = cus * (resident < pa::kDecodeWavesPerCu ? resident : pa::kDecodeWavesPerCu);
+  if (pa::gqa_supported(dtype, head_dim, group) || resident < pa::kDecodeWavesPerCu)
+    *out = cus * (resident < pa::kDecodeWavesPerCu ? resident : pa::kDecodeWavesPerCu);
+  else
+    *out = cus * pa::kVectorWorkersPerCuX8 / 8;
   return PA_OK;
 }
 

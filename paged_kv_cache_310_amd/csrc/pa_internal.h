@@ -201,13 +201,19 @@ hipError_t launch_copy(void* k_cache, void* v_cache, const int64_t* block_mappin
 // blocks and the tails of the same sequences meet in an XCD's L2 only while
 // enough workers run at once.
 constexpr int kWavesPerCu = 4;
-// Workers per CU of pa_decode.  Measured interleaved against 4: 1.1% faster
-// on the long-context batch, 1.9% on the OPT-shaped one, 0.4-0.9% on the
-// grouped-query Pareto batches and 3% on mid-size batches (fewer split
-// segments to merge, fewer concurrent tile streams).  Plain decode of a batch
-// whose sequences share prefix blocks was 9.5% slower at 3 (sharers re-read
-// the prefix through L2 only while enough workers run at once); such batches
-// are what pa_decode_shared is for.
+// Workers per CU of pa_decode on the matrix cores (grouped queries).
+// Measured interleaved against 4: 0.4-0.9% faster on the grouped-query
+// Pareto batches and 3% on mid-size batches (fewer split segments to merge,
+// fewer concurrent tile streams); 704-736 or 800-896 workers (uneven per CU)
+// were 1.5-7% slower than 768.  Plain decode of a batch whose sequences
+// share prefix blocks was 9.5% slower at 3 than at 4 (sharers re-read the
+// prefix through L2 only while enough workers run at once); such batches are
+// what pa_decode_shared is for.
 constexpr int kDecodeWavesPerCu = 3;
+// Workers per CU of the vector decode kernel, in eighths: 21 / 8 (672 on 256
+// CUs).  Swept interleaved from 576 to 768 workers: 672-704 were best, 1.6%
+// faster than 768 on the long-context batch and 1.5% on the OPT-shaped one
+// (fewer concurrent tile streams), 640 equal to 768, 576 8% slower.
+constexpr int kVectorWorkersPerCuX8 = 21;
 
 }  // namespace pa
