@@ -166,8 +166,8 @@ int pa_decode_default_workers(int* num_workers);
  *     slot of position context_lens[s]-1 of sequence s.
  *   workspace      see pa_decode_workspace_size (read/written)
  *   num_workers    0 = default: workers resident at once (3 per compute
- *                  unit on the matrix-core kernel, 21 per 8 compute units
- *                  on the vector kernel), but at most P per segment -- a (sequence,
+ *                  unit; 21 per 8 compute units on the vector kernel with
+ *                  tables of 8k tokens or more), but at most P per segment -- a (sequence,
  *                  KV head) pair on the matrix-core kernel, a (sequence,
  *                  query head) pair otherwise -- rounded up to a multiple of
  *                  8, so that small batches do not spend more time merging

@@ -152,10 +152,7 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
   if (pa::decode_resident_per_cu(dtype, head_dim, block_size, group, &resident) != hipSuccess ||
       resident <= 0)
     return PA_ERR_HIP;
-  if (pa::gqa_supported(dtype, head_dim, group) || resident < pa::kDecodeWavesPerCu)
-    *out = cus * (resident < pa::kDecodeWavesPerCu ? resident : pa::kDecodeWavesPerCu);
-  else
-    *out = cus * pa::kVectorWorkersPerCuX8 / 8;
+  *out = cus * (resident < pa::kDecodeWavesPerCu ? resident : pa::kDecodeWavesPerCu);
   return PA_OK;
 }
 
@@ -194,6 +191,14 @@ int default_workers_for_call(int dtype, int head_dim, int block_size, int max_bl
   if (sb != PA_OK) return sb;
   if (chunks >= kLongTableChunks && kLongTablePieces * segments * 2 <= bound)
     pieces = kLongTablePieces;
+  // Long tables on the vector kernel: fewer workers (see kVectorWorkersPerCuX8).
+  if (chunks >= pa::kVectorLongTableChunks && !pa::gqa_supported(dtype, head_dim, group)) {
+    int cus = 0;
+    const int sc = current_device_cus(&cus);
+    if (sc != PA_OK) return sc;
+    const int fewer = cus * pa::kVectorWorkersPerCuX8 / 8;
+    if (fewer < workers) workers = fewer;
+  }
   int64_t cap = pieces * segments;
   cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;
   *out = cap < workers ? (int)(cap > 0 ? cap : 1) : workers;

@@ -210,10 +210,15 @@ constexpr int kWavesPerCu = 4;
 // prefix through L2 only while enough workers run at once); such batches are
 // what pa_decode_shared is for.
 constexpr int kDecodeWavesPerCu = 3;
-// Workers per CU of the vector decode kernel, in eighths: 21 / 8 (672 on 256
-// CUs).  Swept interleaved from 576 to 768 workers: 672-704 were best, 1.6%
-// faster than 768 on the long-context batch and 1.5% on the OPT-shaped one
-// (fewer concurrent tile streams), 640 equal to 768, 576 8% slower.
+// Workers per CU of the vector decode kernel on tables of at least
+// kVectorLongTableChunks 16-token chunks (8k tokens), in eighths: 21 / 8 (672
+// on 256 CUs).  Swept interleaved in one process from 576 to 768 workers:
+// 672-704 were best on the long-context batch (1.6% faster than 768) and on
+// the OPT-shaped one (1.5%), 576 8% slower.  Timed as bench runs, one
+// process per count, the long-context batch kept 0.6-0.9% of that and the
+// OPT-shaped batch (2k-token table) lost 1.3%, so shorter tables keep three
+// per CU.
 constexpr int kVectorWorkersPerCuX8 = 21;
+constexpr int64_t kVectorLongTableChunks = 512;
 
 }  // namespace pa
