@@ -36,9 +36,13 @@ static_assert(sizeof(MergeRecord) == 48, "merge record layout");
 
 // Work units a segment costs in the split besides its chunks (one unit per
 // chunk), per attention kernel: about the measured per-segment time over the
-// per-chunk time, then tuned by timing.
+// per-chunk time, then tuned by timing.  On the matrix cores 3 beat 2 by
+// 1.5-1.8% (Pareto batches, interleaved in one process) and 0.5-1.9% (bench
+// runs); 1 and 4 were slower than 3.  The vector kernel's 1 and 3 tied 2.
 constexpr int kSegCostValu = 2;
-constexpr int kSegCostMfma = 2;
+constexpr int kSegCostMfma = 3;
+// The shared-prefix kernel's lines (3 was within 1% of 2 there).
+constexpr int kSegCostShared = 2;
 
 // Everything the decode kernels read, in one POD passed by value.
 struct DecodeArgs {

@@ -647,7 +647,7 @@ hipError_t launch_decode_shared(const DecodeArgs& args, const ShareArgs& sh, int
   DecodeArgs a = args;
   a.heads_per_seg = a.group;
   a.piece_rows = kSharedPieceRows;
-  a.seg_cost = kSegCostMfma;
+  a.seg_cost = kSegCostShared;
   if (block_size == 16)
     hipExtLaunchKernelGGL((decode_shared_kernel<16>), dim3(workers), dim3(64), 0, stream, before,
                           after, 0, a, sh);
