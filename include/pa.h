@@ -167,17 +167,14 @@ int pa_decode_default_workers(int* num_workers);
  *   workspace      see pa_decode_workspace_size (read/written)
  *   num_workers    0 = default: workers resident at once (3 per compute
  *                  unit; 21 per 8 compute units on the vector kernel with
- *                  tables of 8k tokens or more), but at most P per segment -- a (sequence,
- *                  KV head) pair on the matrix-core kernel, a (sequence,
- *                  query head) pair otherwise -- rounded up to a multiple of
- *                  8, so that small batches do not spend more time merging
- *                  split pieces than they gain.  P = max_blocks_per_seq *
- *                  block_size / 128 (one piece per 8 16-token chunks of the
- *                  table width), clamped to [16, 48]; 64 for tables of
- *                  1,024+ chunks (16k tokens) when 64 per segment stays
- *                  within half the resident workers.  Otherwise the exact
- *                  number of workers.  A tuning knob that changes only the
- *                  fp32 summation order.
+ *                  tables of 8k tokens or more), but at most about
+ *                  7 sqrt(T), T = segments x 16-token chunks of the table
+ *                  width (a segment is a (sequence, KV head) pair on the
+ *                  matrix-core kernel, a (sequence, query head) pair
+ *                  otherwise), rounded up to a multiple of 8, so that small
+ *                  batches do not spend more time merging split pieces than
+ *                  they gain.  Otherwise the exact number of workers.  A
+ *                  tuning knob that changes only the fp32 summation order.
  * Contract: 0 <= context_lens[s] <= max_blocks_per_seq * block_size; table
  * entries for the blocks a sequence uses lie in [0, num_blocks); entries past
  * them are never read. */

@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/pa.h: argument checks, optional
 // index validation (PA_CHECK=1), workspace sizing and kernel dispatch.
+#include <cmath>
 #include <stdlib.h>
 #include <string.h>
 
@@ -156,24 +157,20 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
   return PA_OK;
 }
 
-// Default workers of one call: the variant's count, but at most P workers
-// per segment (a (sequence, head) pair of the attention kernel's line),
-// rounded up to a multiple of the XCD count.  A segment split over more
-// workers gains little kernel time and costs the merge more piece loads.
-// With one sequence and 8 KV heads, 1,024 workers (128 pieces per segment)
-// took 44 us per step at a 4k context, against 19 us at 384.  Short
-// contexts do best with fewer pieces (32 at 4k).  The host knows only the
-// table width, an upper bound of every context, so P = one piece per 8
-// 16-token chunks of that width, clamped to [16, 48].  Tables of 1,024
-// chunks (16k tokens) or more take 64 pieces while that stays within half
-// of CUs x kWavesPerCu workers: one sequence at 16k-64k then gains 5-14% of
-// its step.  At 8k, or with the device already full (two sequences at 16k or
-// 32k), the extra pieces cost more merge time than they save.
-constexpr int64_t kChunksPerPiece = 8;
-constexpr int64_t kMinPiecesPerSegment = 16;
-constexpr int64_t kMaxPiecesPerSegment = 48;
-constexpr int64_t kLongTableChunks = 1024;
-constexpr int64_t kLongTablePieces = 64;
+// Default workers of one call: the variant's count, or fewer for small
+// batches: about 7 sqrt(T) workers for T = segments x 16-token chunks of the
+// table width (a segment is a (sequence, head) pair of the attention
+// kernel's line; the table width is the host's only bound on the contexts).
+// A segment split over more workers gains kernel time but costs the merge
+// more pieces, and the best chunks per worker grow with the batch: swept
+// over one to four 64/8-head sequences of 1k-64k tokens, 8/8 heads at 8k and
+// 32k and 32/4 heads at 32k (128-768 workers, interleaved), the best count
+// was 192 at T = 1,024 chunks, 384 at 2,048 and 4,096, 640 at 8,192 and
+// 640-768 beyond; 7 sqrt(T) lands within 0-4% of the best on every one
+// (the rule it replaced, 16-64 pieces per segment from the table width, was
+// up to 24% slower at 32k on 4 KV heads and 17% on 8 heads of the vector
+// kernel).  Shorter batches are flat in the count.
+constexpr double kWorkersPerSqrtChunk = 7.0;
 int default_workers_for_call(int dtype, int head_dim, int block_size, int max_blocks_per_seq,
                              int num_seqs, int num_q_heads, int num_kv_heads, int* out) {
   const int group = num_q_heads / num_kv_heads;
@@ -183,14 +180,6 @@ int default_workers_for_call(int dtype, int head_dim, int block_size, int max_bl
   const int64_t segments =
       (int64_t)num_seqs * (pa::gqa_supported(dtype, head_dim, group) ? num_kv_heads : num_q_heads);
   const int64_t chunks = (int64_t)max_blocks_per_seq * block_size / 16;
-  int64_t pieces = chunks / kChunksPerPiece;
-  pieces = pieces < kMinPiecesPerSegment ? kMinPiecesPerSegment : pieces;
-  pieces = pieces > kMaxPiecesPerSegment ? kMaxPiecesPerSegment : pieces;
-  int bound = 0;
-  const int sb = default_workers_for_current_device(&bound);
-  if (sb != PA_OK) return sb;
-  if (chunks >= kLongTableChunks && kLongTablePieces * segments * 2 <= bound)
-    pieces = kLongTablePieces;
   // Long tables on the vector kernel: fewer workers (see kVectorWorkersPerCuX8).
   if (chunks >= pa::kVectorLongTableChunks && !pa::gqa_supported(dtype, head_dim, group)) {
     int cus = 0;
@@ -199,15 +188,22 @@ int default_workers_for_call(int dtype, int head_dim, int block_size, int max_bl
     const int fewer = cus * pa::kVectorWorkersPerCuX8 / 8;
     if (fewer < workers) workers = fewer;
   }
-  int64_t cap = pieces * segments;
+  const double t = (double)segments * (double)(chunks > 0 ? chunks : 1);
+  int64_t cap = (int64_t)(kWorkersPerSqrtChunk * std::sqrt(t));
   cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;
-  *out = cap < workers ? (int)(cap > 0 ? cap : 1) : workers;
+  if (cap < pa::kNumXcd) cap = pa::kNumXcd;
+  *out = cap < workers ? (int)cap : workers;
   return PA_OK;
 }
 
 // Default workers of a shared-prefix call: every worker of the shared
-// kernel resident at once, capped per segment like pa_decode with the tail
-// line's (sequence, KV head) segments.
+// kernel resident at once, but at most P per tail-line (sequence, KV head)
+// segment: P = one piece per 8 16-token chunks of the table width, clamped to
+// [16, 48] (the rule pa_decode used before its square-root one; the shared
+// kernel's batches have many segments, where the cap rarely binds).
+constexpr int64_t kChunksPerPiece = 8;
+constexpr int64_t kMinPiecesPerSegment = 16;
+constexpr int64_t kMaxPiecesPerSegment = 48;
 int default_workers_for_shared(int block_size, int max_blocks_per_seq, int num_seqs,
                                int num_kv_heads, int* out) {
   int cus = 0;
