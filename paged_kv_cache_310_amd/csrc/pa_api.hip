@@ -669,11 +669,15 @@ constexpr int kPrefillMaxSplits = 32;
 constexpr int kPrefillWgsPerCu = 3;        // resident prefill workgroups per CU
 constexpr int kPrefillMinStepsPerSplit = 8;
 constexpr int kPrefillBalancedMaxSplits = 16;   // cap of the balanced choice
+constexpr int kPrefillSplitWgsPerCu = 2;        // target of the many-split choice
 
 // Splits pa_prefill_split picks for num_splits = 0.  None while the row tiles
 // alone fill the device's workgroup slots (3 per compute unit) twice.  When
-// even 16 splits would not fill one round of slots, as many as fill it (at
-// most 32).  Otherwise S in [2, Smax], Smax = floor(2 slots / tiles) (at
+// even 16 splits would not fill one round of slots, as many as make two
+// workgroups per compute unit (at most 32): on one 64/8-head sequence's
+// 64-token chunk over 32k, 16 splits (512 workgroups) took 89.4 us against
+// 92.3 at 24 (a full round), and on 40 heads' 64-token chunk over 32k, 12
+// (480) took 134.7 us against 161.8-186.2 at 20-32.  Otherwise S in [2, Smax], Smax = floor(2 slots / tiles) (at
 // least 2, at most 16), with the smallest per-CU share ceil(tiles S / CUs) / S
 // of one tile's work -- splits that leave some CUs a workgroup more than
 // others lose -- and among equal shares the most splits (more resident
@@ -692,7 +696,7 @@ int prefill_auto_splits(int num_seqs, int max_query_len, int group, int num_kv_h
   const int64_t by_steps = max_steps / kPrefillMinStepsPerSplit;
   int64_t best = 1;
   if (wgs > 0 && wgs * kPrefillBalancedMaxSplits <= slots) {
-    best = slots / wgs;
+    best = (int64_t)cus * kPrefillSplitWgsPerCu / wgs;
     best = best < kPrefillMaxSplits ? best : kPrefillMaxSplits;
   } else if (wgs > 0 && wgs < 2 * slots) {
     int64_t smax = 2 * slots / wgs;
