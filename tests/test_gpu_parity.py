@@ -79,11 +79,13 @@ def test_worker_counts(workers, group):
 
 @pytest.mark.parametrize("dtype,d,hq,hkv", [(wl.FP32, 64, 4, 4), (wl.FP32, 128, 4, 4),
                                              (wl.BF16, 64, 4, 4), (wl.BF16, 128, 16, 2)])
-@pytest.mark.parametrize("per_segment", [15, 16, 64])
+@pytest.mark.parametrize("per_segment", [15, 16, 64, 96, 160])
 def test_merge_of_many_pieces(dtype, d, hq, hkv, per_segment):
     """One long and one short sequence with many workers per segment: from 16
     per segment on, segments are merged by a workgroup each (every wave folds a
-    quarter of the pieces); 15 stays on the one-wave merge."""
+    quarter of the pieces, in rounds of 16 past 64 pieces); 15 stays on the
+    one-wave merge.  96 and 160 per segment are what the default worker count
+    gives one sequence at 32k with 8 and 4 KV heads."""
     say("many pieces", dtype, d, hq, hkv, per_segment)
     w = small(dtype, d, 16, hq, hkv, lens=[3000, 40], seed=13)
     segments = 2 * (hkv if hq != hkv and dtype == wl.BF16 and d == 128 else hq)
