@@ -14,8 +14,7 @@
 // workgroups share its K/V in one L2.  A row is a (query token, query head)
 // pair of the KV head's group, token-major, so grouped query heads share
 // every K/V tile.  Each wave owns 32 consecutive rows as two 16-row MFMA
-// tiles.  The workgroup walks the keys in
-// steps of 32 (two 16-token halves).  A step's K and V rows go from the pool
+// tiles.  The workgroup walks the keys in steps of 32 (two 16-token halves).  A step's K and V rows go from the pool
 // straight into one of two LDS buffers (buffer loads with an LDS destination,
 // no trip through registers), issued one step ahead, so they arrive while the
 // step before is computed; one barrier per step publishes them.  The
@@ -40,12 +39,12 @@
 //    running sum adds the same rounded values (v_dot2_f32_bf16 with (1, 1)).
 //  * O^T[128 dims x 16 rows] += V^T . P^T, eight v_mfma_f32_16x16x32_bf16
 //    (one per c = 0..7) per row tile, issued after both tiles' softmax so
-//    that one V^T operand read serves both tiles.  The 32 keys of the k-dimension are ordered so that
-//    lane l's eight P values are exactly its B operand: k = 8g+i is key 4g+i
-//    and k = 8g+4+i is key 16+4g+i.  The A operand of MFMA c (dims
+//    that one V^T operand read serves both tiles.  The 32 keys of the
+//    k-dimension are ordered so that lane l's eight P values are exactly its
+//    B operand: k = 8g+i is key 4g+i and k = 8g+4+i is key 16+4g+i.  The A operand of MFMA c (dims
 //    16c..16c+15) comes from two transposing LDS reads (ds_read_b64_tr_b16)
-//    of the row-major V tile, so lane l ends up holding dims 16c + 4g + i of
-//    row n.
+//    of the V tile (its LDS layout is below), so lane l ends up holding dims
+//    16c + 4g + i of row n.
 #include "decode_common.h"
 
 namespace pa {
