@@ -79,6 +79,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle-s", type=float, default=0.3,
+                   help="untimed steps for this many seconds before the warm-up steps")
     p.add_argument("--workload", default="llama13b_long")
     p.add_argument("--workers", type=int, default=0, help="decode workers (0 = library default)")
     p.add_argument("--plain", action="store_true",
@@ -370,6 +372,16 @@ def main():
         if ev is not None:
             pa.pa_set_decode_events(None, None)
 
+    # Settle: after a process starts issuing work, the first few dozen decode
+    # launches run 5-20% slower than the rest (a transient of the device's
+    # clocks under the new load, a few milliseconds long; it shows in every
+    # kernel trace), so the run first steps untimed for settle_s seconds and
+    # a short run's few warm-up steps still lead into the steady state.
+    t_settle = time.perf_counter() + max(args.settle_s, 0.0)
+    while time.perf_counter() < t_settle:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -433,6 +445,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle_s,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
