@@ -166,8 +166,8 @@ int pa_decode_default_workers(int* num_workers);
  *     slot of position context_lens[s]-1 of sequence s.
  *   workspace      see pa_decode_workspace_size (read/written)
  *   num_workers    0 = default: workers resident at once (3 per compute
- *                  unit; 21 per 8 compute units on the vector kernel with
- *                  tables of 8k tokens or more), but at most about
+ *                  unit on the matrix-core kernel, 21 per 8 compute units on
+ *                  the vector kernel), but at most about
  *                  7 sqrt(T), T = segments x 16-token chunks of the table
  *                  width (a segment is a (sequence, KV head) pair on the
  *                  matrix-core kernel, a (sequence, query head) pair

@@ -153,7 +153,10 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
   if (pa::decode_resident_per_cu(dtype, head_dim, block_size, group, &resident) != hipSuccess ||
       resident <= 0)
     return PA_ERR_HIP;
-  *out = cus * (resident < pa::kDecodeWavesPerCu ? resident : pa::kDecodeWavesPerCu);
+  if (pa::gqa_supported(dtype, head_dim, group) || resident < pa::kDecodeWavesPerCu)
+    *out = cus * (resident < pa::kDecodeWavesPerCu ? resident : pa::kDecodeWavesPerCu);
+  else
+    *out = cus * pa::kVectorWorkersPerCuX8 / 8;
   return PA_OK;
 }
 
@@ -180,14 +183,6 @@ int default_workers_for_call(int dtype, int head_dim, int block_size, int max_bl
   const int64_t segments =
       (int64_t)num_seqs * (pa::gqa_supported(dtype, head_dim, group) ? num_kv_heads : num_q_heads);
   const int64_t chunks = (int64_t)max_blocks_per_seq * block_size / 16;
-  // Long tables on the vector kernel: fewer workers (see kVectorWorkersPerCuX8).
-  if (chunks >= pa::kVectorLongTableChunks && !pa::gqa_supported(dtype, head_dim, group)) {
-    int cus = 0;
-    const int sc = current_device_cus(&cus);
-    if (sc != PA_OK) return sc;
-    const int fewer = cus * pa::kVectorWorkersPerCuX8 / 8;
-    if (fewer < workers) workers = fewer;
-  }
   const double t = (double)segments * (double)(chunks > 0 ? chunks : 1);
   int64_t cap = (int64_t)(kWorkersPerSqrtChunk * std::sqrt(t));
   cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;

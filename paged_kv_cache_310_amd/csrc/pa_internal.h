@@ -214,15 +214,14 @@ constexpr int kWavesPerCu = 4;
 // prefix through L2 only while enough workers run at once); such batches are
 // what pa_decode_shared is for.
 constexpr int kDecodeWavesPerCu = 3;
-// Workers per CU of the vector decode kernel on tables of at least
-// kVectorLongTableChunks 16-token chunks (8k tokens), in eighths: 21 / 8 (672
-// on 256 CUs).  Swept interleaved in one process from 576 to 768 workers:
-// 672-704 were best on the long-context batch (1.6% faster than 768) and on
-// the OPT-shaped one (1.5%), 576 8% slower.  Timed as bench runs, one
-// process per count, the long-context batch kept 0.6-0.9% of that and the
-// OPT-shaped batch (2k-token table) lost 1.3%, so shorter tables keep three
-// per CU.
+// Workers per CU of the vector decode kernel, in eighths: 21 / 8 (672 on 256
+// CUs).  Swept interleaved in one process from 576 to 768 workers: 672-704
+// were best on the long-context batch (1.6% faster than 768) and on the
+// OPT-shaped one (1.5%), 576 8% slower.  Bench runs (one process per count,
+// after the settle phase) agree: long-context 6,731-6,739 GB/s at 672,
+// 6,716-6,721 at 704, 6,605-6,616 at 768; OPT-shaped 6,571-6,579 at 672-704
+// against 6,484-6,493 at 768; plain decode of the steady shared-prefix batch
+// 6,838-6,848 at 704, 6,745-6,757 at 672, 6,689-6,700 at 768.
 constexpr int kVectorWorkersPerCuX8 = 21;
-constexpr int64_t kVectorLongTableChunks = 512;
 
 }  // namespace pa
