@@ -101,13 +101,26 @@ def pa_status_string(status: int) -> str:
     return _load().pa_status_string(int(status)).decode()
 
 
+# The current stream's handle as an int, without building a torch Stream
+# object (about 30x cheaper per call); torch.cuda.current_stream otherwise.
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # ctypes passes an int (or None) for a c_void_p argument.
+    return None if t is None else t.data_ptr()
 
 
-def _stream(device: torch.device, stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+def _device_index(device: torch.device) -> int:
+    return device.index if device.index is not None else torch.cuda.current_device()
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is not None:
+        return stream.cuda_stream
+    if _current_raw_stream is not None:
+        return _current_raw_stream(_device_index(device))
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -124,10 +137,10 @@ def _need(cond: bool, msg: str) -> None:
 def _check_cache(k_cache: torch.Tensor, v_cache: torch.Tensor):
     _need(k_cache.is_cuda and k_cache.dim() == 4 and k_cache.is_contiguous(),
           "k_cache must be a contiguous CUDA tensor [num_blocks, num_kv_heads, block_size, head_dim]")
-    _need(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype
-          and v_cache.is_contiguous() and v_cache.device == k_cache.device,
-          "v_cache must match k_cache")
-    return k_cache.shape
+    shape = k_cache.shape
+    _need(v_cache.dtype == k_cache.dtype and v_cache.shape == shape and v_cache.is_contiguous()
+          and v_cache.get_device() == k_cache.get_device(), "v_cache must match k_cache")
+    return shape
 
 
 def _call(name: str, status: int) -> None:
@@ -140,10 +153,12 @@ def pa_append_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> N
     nb, hkv, bs, d = _check_cache(k_cache, v_cache)
     t = slot_mapping.numel()
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
-          and slot_mapping.device == k_cache.device, "slot_mapping must be int64 on the pool device")
+          and slot_mapping.get_device() == k_cache.get_device(),
+          "slot_mapping must be int64 on the pool device")
     for x in (k_new, v_new):
         _need(x.shape == (t, hkv, d) and x.dtype == k_cache.dtype and x.is_contiguous()
-              and x.device == k_cache.device, "k_new/v_new must be [num_tokens, num_kv_heads, head_dim]")
+              and x.get_device() == k_cache.get_device(),
+              "k_new/v_new must be [num_tokens, num_kv_heads, head_dim]")
     _call("pa_append_kv", _load().pa_append_kv(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), t, nb, hkv,
         bs, d, _dtype_code(k_cache), _stream(k_cache.device, stream)))
@@ -153,7 +168,7 @@ def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
     """Copy whole blocks ``(src, dst)`` of both pools."""
     nb, hkv, bs, d = _check_cache(k_cache, v_cache)
     _need(block_mapping.dtype == torch.int64 and block_mapping.is_contiguous()
-          and block_mapping.device == k_cache.device and block_mapping.numel() % 2 == 0,
+          and block_mapping.get_device() == k_cache.get_device() and block_mapping.numel() % 2 == 0,
           "block_mapping must be int64 [num_pairs, 2] on the pool device")
     _call("pa_copy_blocks", _load().pa_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), block_mapping.numel() // 2, nb, hkv, bs,
@@ -168,7 +183,8 @@ def _layer_pools(k_caches, v_caches):
     shape = _check_cache(k_caches[0], v_caches[0])
     for k, v in zip(k_caches, v_caches):
         _need(_check_cache(k, v) == shape and k.dtype == k_caches[0].dtype
-              and k.device == k_caches[0].device, "every layer's pools must match layer 0's")
+              and k.get_device() == k_caches[0].get_device(),
+              "every layer's pools must match layer 0's")
     return shape, _ptr_array(k_caches), _ptr_array(v_caches)
 
 
@@ -188,11 +204,13 @@ def pa_append_kv_layers(k_caches, v_caches, k_new, v_new, slot_mapping, stream=N
     ref = k_caches[0]
     t = slot_mapping.numel()
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
-          and slot_mapping.device == ref.device, "slot_mapping must be int64 on the pool device")
+          and slot_mapping.get_device() == ref.get_device(),
+          "slot_mapping must be int64 on the pool device")
     _need(len(k_new) == layers and len(v_new) == layers, "one k_new and one v_new per layer")
     for x in list(k_new) + list(v_new):
         _need(x.shape == (t, hkv, d) and x.dtype == ref.dtype and x.is_contiguous()
-              and x.device == ref.device, "k_new/v_new must be [num_tokens, num_kv_heads, head_dim]")
+              and x.get_device() == ref.get_device(),
+              "k_new/v_new must be [num_tokens, num_kv_heads, head_dim]")
     _call("pa_append_kv_layers", _load().pa_append_kv_layers(
         kp, vp, _ptr_array(k_new), _ptr_array(v_new), layers, _ptr(slot_mapping), t, nb, hkv, bs,
         d, _dtype_code(ref), _stream(ref.device, stream)))
@@ -204,7 +222,7 @@ def pa_copy_blocks_layers(k_caches, v_caches, block_mapping, stream=None) -> Non
     (nb, hkv, bs, d), kp, vp = _layer_pools(k_caches, v_caches)
     ref = k_caches[0]
     _need(block_mapping.dtype == torch.int64 and block_mapping.is_contiguous()
-          and block_mapping.device == ref.device and block_mapping.numel() % 2 == 0,
+          and block_mapping.get_device() == ref.get_device() and block_mapping.numel() % 2 == 0,
           "block_mapping must be int64 [num_pairs, 2] on the pool device")
     _call("pa_copy_blocks_layers", _load().pa_copy_blocks_layers(
         kp, vp, len(k_caches), _ptr(block_mapping), block_mapping.numel() // 2, nb, hkv, bs, d,
@@ -217,6 +235,22 @@ def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
     _call("pa_decode_workspace_size", _load().pa_decode_workspace_size(
         num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers, ctypes.byref(out)))
     return int(out.value)
+
+
+# Workspace sizes by (current device, sizes): the size is a pure function of
+# them (the default worker count depends on the device's compute units).
+_workspace_sizes = {}
+
+
+def _decode_need(size_fn, device_index: int, b: int, hq: int, hkv: int, d: int,
+                 num_workers: int) -> int:
+    key = (size_fn, device_index, b, hq, hkv, d, num_workers)
+    need = _workspace_sizes.get(key)
+    if need is None:
+        with torch.cuda.device(device_index):
+            need = size_fn(b, hq, hkv, d, num_workers)
+        _workspace_sizes[key] = need
+    return need
 
 
 def pa_decode_default_workers() -> int:
@@ -253,7 +287,8 @@ def pa_read_probe(base, tile_ids=None, tile_bytes: int = 4096, nontemporal: bool
     nbytes = base.numel() * base.element_size()
     if tile_ids is not None:
         _need(tile_ids.dtype == torch.int32 and tile_ids.dim() == 1 and tile_ids.is_contiguous()
-              and tile_ids.device == base.device, "tile_ids must be a 1-D int32 tensor on base's device")
+              and tile_ids.get_device() == base.get_device(),
+              "tile_ids must be a 1-D int32 tensor on base's device")
         n = tile_ids.numel()
     else:
         n = nbytes // tile_bytes if num_tiles is None else int(num_tiles)
@@ -274,19 +309,22 @@ def decode_workspace(device, nbytes: int, stream=None) -> torch.Tensor:
     are not.  The buffer is allocated while ``stream`` is current, so when a
     larger one replaces it, torch's caching allocator hands the old memory
     out again only in that stream's order, after the calls that used it."""
-    device = torch.device(device)
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    key = (device.type, device.index, int(s.cuda_stream))
+    if not isinstance(device, torch.device):
+        device = torch.device(device)
+    index = _device_index(device)
+    key = (index, _stream(device, stream))   # the stream handle last
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        s = torch.cuda.current_stream(index) if stream is None else stream
         with torch.cuda.stream(s):
-            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=index)
         _workspaces[key] = ws
     return ws
 
 
 def _check_workspace(workspace: torch.Tensor, ref: torch.Tensor) -> None:
-    _need(workspace.is_cuda and workspace.is_contiguous() and workspace.device == ref.device,
+    _need(workspace.is_cuda and workspace.is_contiguous()
+          and workspace.get_device() == ref.get_device(),
           "workspace must be a contiguous device tensor on q's device")
 
 
@@ -295,28 +333,37 @@ def _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, out, k_n
     """Checks pa_decode's tensors; returns the pool shape and ``out`` (made
     when not given)."""
     nb, hkv, bs, d = _check_cache(k_cache, v_cache)
-    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == k_cache.dtype and q.is_contiguous()
-          and q.device == k_cache.device, "q must be [num_seqs, num_q_heads, head_dim] like the pools")
-    b, hq, _ = q.shape
+    dev = k_cache.get_device()
+    dt = k_cache.dtype
+    _need(q.dim() == 3 and q.dtype == dt and q.is_contiguous() and q.get_device() == dev,
+          "q must be [num_seqs, num_q_heads, head_dim] like the pools")
+    b, hq, qd = q.shape
+    _need(qd == d, "q must be [num_seqs, num_q_heads, head_dim] like the pools")
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
           and block_tables.shape[0] == b and block_tables.is_contiguous()
-          and block_tables.device == q.device, "block_tables must be int32 [num_seqs, max_blocks]")
-    _need(context_lens.dtype == torch.int32 and context_lens.shape == (b,)
-          and context_lens.is_contiguous() and context_lens.device == q.device,
+          and block_tables.get_device() == dev, "block_tables must be int32 [num_seqs, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1
+          and context_lens.shape[0] == b and context_lens.is_contiguous()
+          and context_lens.get_device() == dev,
           "context_lens must be a contiguous int32 [num_seqs] tensor")
-    fused = [x is not None for x in (k_new, v_new, slot_mapping)]
-    _need(all(fused) or not any(fused), "k_new, v_new and slot_mapping go together")
-    if all(fused):
+    if k_new is not None and v_new is not None and slot_mapping is not None:
+        row = (b, hkv, d)
         for x in (k_new, v_new):
-            _need(x.shape == (b, hkv, d) and x.dtype == q.dtype and x.is_contiguous()
-                  and x.device == q.device, "k_new/v_new must be [num_seqs, num_kv_heads, head_dim]")
-        _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (b,)
-              and slot_mapping.is_contiguous() and slot_mapping.device == q.device,
+            _need(x.dtype == dt and tuple(x.shape) == row and x.is_contiguous()
+                  and x.get_device() == dev,
+                  "k_new/v_new must be [num_seqs, num_kv_heads, head_dim]")
+        _need(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1
+              and slot_mapping.shape[0] == b and slot_mapping.is_contiguous()
+              and slot_mapping.get_device() == dev,
               "slot_mapping must be a contiguous int64 [num_seqs] tensor")
+    else:
+        _need(k_new is None and v_new is None and slot_mapping is None,
+              "k_new, v_new and slot_mapping go together")
     if out is None:
         out = torch.empty_like(q)
-    _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
-          and out.device == q.device, "out must match q")
+    else:
+        _need(out.dtype == dt and tuple(out.shape) == (b, hq, d) and out.is_contiguous()
+              and out.get_device() == dev, "out must match q")
     return (nb, hkv, bs, d), out
 
 
@@ -327,10 +374,12 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
     (nb, hkv, bs, d), out = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                                out, k_new, v_new, slot_mapping)
     b, hq, _ = q.shape
-    need = pa_decode_workspace_size(b, hq, hkv, d, num_workers)
     if workspace is None:
+        index = q.get_device()
+        need = _decode_need(pa_decode_workspace_size, index, b, hq, hkv, d, num_workers)
         workspace = decode_workspace(q.device, need, stream)
-    _check_workspace(workspace, q)
+    else:
+        _check_workspace(workspace, q)
     _call("pa_decode", _load().pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), b, hq, hkv, d, bs, nb, float(scale),
@@ -361,15 +410,17 @@ def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, scale, gro
     b, hq, _ = q.shape
     _need(group_start.dtype == torch.int32 and group_start.dim() == 1
           and group_start.numel() >= 1 and group_start.is_contiguous()
-          and group_start.device == q.device,
+          and group_start.get_device() == q.get_device(),
           "group_start must be a contiguous int32 [num_groups + 1] tensor on q's device")
     _need(prefix_lens.dtype == torch.int32 and prefix_lens.shape == (b,)
-          and prefix_lens.is_contiguous() and prefix_lens.device == q.device,
+          and prefix_lens.is_contiguous() and prefix_lens.get_device() == q.get_device(),
           "prefix_lens must be a contiguous int32 [num_seqs] tensor on q's device")
-    need = pa_decode_shared_workspace_size(b, hq, hkv, d, num_workers)
     if workspace is None:
+        index = q.get_device()
+        need = _decode_need(pa_decode_shared_workspace_size, index, b, hq, hkv, d, num_workers)
         workspace = decode_workspace(q.device, need, stream)
-    _check_workspace(workspace, q)
+    else:
+        _check_workspace(workspace, q)
     _call("pa_decode_shared", _load().pa_decode_shared(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), b, hq, hkv, d, bs, nb, float(scale),
@@ -420,25 +471,25 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, sca
     ``workspace`` (a uint8 device tensor) is then allocated when not given."""
     nb, hkv, bs, d = _check_cache(k_cache, v_cache)
     _need(q.dim() == 3 and q.shape[2] == d and q.dtype == k_cache.dtype and q.is_contiguous()
-          and q.device == k_cache.device,
+          and q.get_device() == k_cache.get_device(),
           "q must be [num_query_tokens, num_q_heads, head_dim] like the pools")
     t, hq, _ = q.shape
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
-          and block_tables.is_contiguous() and block_tables.device == q.device,
+          and block_tables.is_contiguous() and block_tables.get_device() == q.get_device(),
           "block_tables must be int32 [num_seqs, max_blocks]")
     b = block_tables.shape[0]
     _need(context_lens.dtype == torch.int32 and context_lens.shape == (b,)
-          and context_lens.is_contiguous() and context_lens.device == q.device,
+          and context_lens.is_contiguous() and context_lens.get_device() == q.get_device(),
           "context_lens must be int32 [num_seqs]")
     _need(query_start.dtype == torch.int32 and query_start.shape == (b + 1,)
-          and query_start.is_contiguous() and query_start.device == q.device,
+          and query_start.is_contiguous() and query_start.get_device() == q.get_device(),
           "query_start must be int32 [num_seqs + 1]")
     if max_query_len is None:
         max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if b else 0
     if out is None:
         out = torch.empty_like(q)
     _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
-          and out.device == q.device, "out must match q")
+          and out.get_device() == q.get_device(), "out must match q")
     if num_splits == 1:
         _call("pa_prefill", _load().pa_prefill(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),

@@ -347,7 +347,7 @@ def test_streams_get_their_own_default_workspace():
     for oa, ob in outs:
         assert torch.equal(oa.view(torch.int16), ref_a.view(torch.int16))
         assert torch.equal(ob.view(torch.int16), ref_b.view(torch.int16))
-    keys = {k for k in _binding._workspaces if k[2] in (s1.cuda_stream, s2.cuda_stream)}
+    keys = {k for k in _binding._workspaces if k[-1] in (s1.cuda_stream, s2.cuda_stream)}
     assert len(keys) == 2
 
 
