@@ -167,11 +167,13 @@ int pa_decode_default_workers(int* num_workers);
  *   workspace      see pa_decode_workspace_size (read/written)
  *   num_workers    0 = default: workers resident at once (3 per compute
  *                  unit on the matrix-core kernel, 21 per 8 compute units on
- *                  the vector kernel), but at most about
+ *                  the vector kernel, 3 per compute unit there when T below
+ *                  is under 65,536), but at most about
  *                  7 sqrt(T), T = segments x 16-token chunks of the table
  *                  width (a segment is a (sequence, KV head) pair on the
  *                  matrix-core kernel, a (sequence, query head) pair
- *                  otherwise), rounded up to a multiple of 8, so that small
+ *                  otherwise; the vector kernel's bound is at least 20 per
+ *                  segment), rounded up to a multiple of 8, so that small
  *                  batches do not spend more time merging split pieces than
  *                  they gain.  Otherwise the exact number of workers.  A
  *                  tuning knob that changes only the fp32 summation order.

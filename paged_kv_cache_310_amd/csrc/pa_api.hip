@@ -145,7 +145,10 @@ int default_workers_for_current_device(int* out) {
 }
 
 // Default workers of one kernel variant: every worker resident at once.
-int default_workers_for_variant(int dtype, int head_dim, int block_size, int group, int* out) {
+// `small` (may be null) receives the count for small batches on the vector
+// kernel: the resident count up to kDecodeWavesPerCu per CU.
+int default_workers_for_variant(int dtype, int head_dim, int block_size, int group, int* out,
+                                int* small = nullptr) {
   int cus = 0;
   const int st = current_device_cus(&cus);
   if (st != PA_OK) return st;
@@ -153,10 +156,12 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
   if (pa::decode_resident_per_cu(dtype, head_dim, block_size, group, &resident) != hipSuccess ||
       resident <= 0)
     return PA_ERR_HIP;
+  const int per_cu = resident < pa::kDecodeWavesPerCu ? resident : pa::kDecodeWavesPerCu;
   if (pa::gqa_supported(dtype, head_dim, group) || resident < pa::kDecodeWavesPerCu)
-    *out = cus * (resident < pa::kDecodeWavesPerCu ? resident : pa::kDecodeWavesPerCu);
+    *out = cus * per_cu;
   else
     *out = cus * pa::kVectorWorkersPerCuX8 / 8;
+  if (small != nullptr) *small = cus * per_cu;
   return PA_OK;
 }
 
@@ -174,17 +179,32 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
 // up to 24% slower at 32k on 4 KV heads and 17% on 8 heads of the vector
 // kernel).  Shorter batches are flat in the count.
 constexpr double kWorkersPerSqrtChunk = 7.0;
+// The vector kernel's segments are single query heads, so its pieces are a
+// head's row, and many heads per sequence give many short segments.  Below
+// kVectorSmallBatch chunks of T it takes 3 workers per CU (not 21 per 8 CUs)
+// and at least kVectorPiecesPerSegment pieces per segment under the cap.
+// Swept on 32- and 40-head sequences of 1k-16k tokens (T = 2,560-40,960):
+// 768 workers were the fastest count on each, 2-13% faster than the earlier
+// default (352 at 1k, 672 beyond); at T = 82k 672 and 768 tie, and from
+// 164k (the OPT-shaped batch) 672 is 1-1.6% faster.
+constexpr double kVectorSmallBatch = 65536.0;
+constexpr int64_t kVectorPiecesPerSegment = 20;
 int default_workers_for_call(int dtype, int head_dim, int block_size, int max_blocks_per_seq,
                              int num_seqs, int num_q_heads, int num_kv_heads, int* out) {
   const int group = num_q_heads / num_kv_heads;
-  int workers = 0;
-  const int st = default_workers_for_variant(dtype, head_dim, block_size, group, &workers);
+  int workers = 0, small = 0;
+  const int st = default_workers_for_variant(dtype, head_dim, block_size, group, &workers, &small);
   if (st != PA_OK) return st;
-  const int64_t segments =
-      (int64_t)num_seqs * (pa::gqa_supported(dtype, head_dim, group) ? num_kv_heads : num_q_heads);
+  const bool mfma = pa::gqa_supported(dtype, head_dim, group);
+  const int64_t segments = (int64_t)num_seqs * (mfma ? num_kv_heads : num_q_heads);
   const int64_t chunks = (int64_t)max_blocks_per_seq * block_size / 16;
   const double t = (double)segments * (double)(chunks > 0 ? chunks : 1);
   int64_t cap = (int64_t)(kWorkersPerSqrtChunk * std::sqrt(t));
+  if (!mfma && t < kVectorSmallBatch) {
+    workers = small > workers ? small : workers;
+    const int64_t floor = kVectorPiecesPerSegment * segments;
+    cap = floor > cap ? floor : cap;
+  }
   cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;
   if (cap < pa::kNumXcd) cap = pa::kNumXcd;
   *out = cap < workers ? (int)cap : workers;
