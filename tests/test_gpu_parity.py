@@ -428,3 +428,15 @@ def test_workload_gqa_single_sequence(cache, name):
     merged (the default worker count is capped per segment)."""
     w = _full(cache, name)
     _check_full(w, rows=[(0, h) for h in range(w.num_q_heads)])
+
+
+@pytest.mark.parametrize("hq,lens", [(40, [1024]), (40, [4096]), (40, [4096, 4096]),
+                                     (32, [8192]), (8, [32768])],
+                         ids=["40h-1k", "40h-4k", "40h-2x4k", "32h-8k", "8h-32k"])
+def test_small_multi_head_batches(hq, lens):
+    """Small batches on the vector kernel take 3 workers per CU by default,
+    so each head's segment is split into many pieces (20 to 96 here): every
+    output row against the oracle, pools bit-exact after the fused append."""
+    w = wl.make_simple("mha_small", 11, wl.BF16, hq, hq, 128, 16, lens, append=True, poison=True)
+    rows = [(s, h) for s in range(w.num_seqs) for h in range(w.num_q_heads)]
+    _check_full(w, rows=rows)
