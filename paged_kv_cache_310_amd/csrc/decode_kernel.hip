@@ -300,10 +300,24 @@ __global__ __launch_bounds__(64, (min_waves<T, D>())) void decode_valu_kernel(co
 constexpr int kMergeBatch = 8;
 constexpr int kMergeWideFrom = 16;
 
+// Merge workgroups are placed on the XCD that ran the decode workers whose
+// records they fold: the attention launch puts workers
+// [x * workers / 8, (x + 1) * workers / 8) on XCD x, so a segment's pieces,
+// written by consecutive workers, and its record are still in that XCD's L2
+// (when the worker count divides evenly; otherwise workgroups go in order).
+// Measured interleaved: one 64/8-head sequence 16.6 -> 15.6 us per step at 4k
+// and 33.5 -> 31.7 at 32k; the batched workloads unchanged, outputs identical.
 template <typename T, int D, int kBatch>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const DecodeArgs a, int workers) {
   const int lane = threadIdx.x % 64;
-  const int id = uniform((int)(blockIdx.x * kMergeWaves + threadIdx.x / 64));
+  constexpr int HPW = merge_heads_per_wave<D>();
+  const int wpr = (a.heads_per_seg + HPW - 1) / HPW;   // waves per record
+  const int xw = workers / kNumXcd * wpr;              // waves per XCD
+  const bool by_xcd = workers % kNumXcd == 0 && xw % kMergeWaves == 0;
+  const int id = uniform(by_xcd ? (int)(blockIdx.x % kNumXcd) * xw +
+                                      (int)(blockIdx.x / kNumXcd) * kMergeWaves +
+                                      (int)(threadIdx.x / 64)
+                                : (int)(blockIdx.x * kMergeWaves + threadIdx.x / 64));
   merge_record_wave<T, D, kBatch>(a, workers, id, lane);
 }
 
@@ -325,7 +339,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_wide_kernel(const Deco
   const int wave = threadIdx.x / 64;
   const int hps = a.heads_per_seg;
   const int wpr = (hps + HPW - 1) / HPW;           // head groups per record
-  const int id = (int)blockIdx.x;
+  // One workgroup per (record, head group), placed by XCD as in merge_kernel.
+  const int id = workers % kNumXcd == 0
+                     ? (int)(blockIdx.x % kNumXcd) * (workers / kNumXcd * wpr) +
+                           (int)(blockIdx.x / kNumXcd)
+                     : (int)blockIdx.x;
   const int w = id / wpr;
   if (w >= workers) return;                        // whole workgroup
   typedef __attribute__((address_space(4))) const MergeRecord const_record;
