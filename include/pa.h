@@ -169,11 +169,13 @@ int pa_decode_default_workers(int* num_workers);
  *                  unit on the matrix-core kernel, 21 per 8 compute units on
  *                  the vector kernel, 3 per compute unit there when T below
  *                  is under 65,536), but at most about
- *                  7 sqrt(T), T = segments x 16-token chunks of the table
- *                  width (a segment is a (sequence, KV head) pair on the
- *                  matrix-core kernel, a (sequence, query head) pair
- *                  otherwise; the vector kernel's bound is at least 20 per
- *                  segment), rounded up to a multiple of 8, so that small
+ *                  10 sqrt(T) (and 160 per segment) on the matrix-core
+ *                  kernel and 7 sqrt(T) on the vector kernel, T = segments
+ *                  x 16-token chunks of the table width (a segment is a
+ *                  (sequence, KV head) pair on the matrix-core kernel, a
+ *                  (sequence, query head) pair otherwise; the vector
+ *                  kernel's bound is at least 20 per segment), rounded up
+ *                  to a multiple of 8, so that small
  *                  batches do not spend more time merging split pieces than
  *                  they gain.  Otherwise the exact number of workers.  A
  *                  tuning knob that changes only the fp32 summation order.

@@ -177,8 +177,16 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
 // 640-768 beyond; 7 sqrt(T) lands within 0-4% of the best on every one
 // (the rule it replaced, 16-64 pieces per segment from the table width, was
 // up to 24% slower at 32k on 4 KV heads and 17% on 8 heads of the vector
-// kernel).  Shorter batches are flat in the count.
+// kernel).  Shorter batches are flat in the count.  Once the merge ran on
+// the XCD whose L2 holds the pieces, the matrix-core kernel's best counts
+// rose: 448 against 320 at one 64/8-head sequence of 4k (15.0 -> 14.3 us),
+// 768 at 16k; so it takes 10 sqrt(T), at most 160 pieces per segment (32/4
+// heads at 32k: 640 beat 768 by 3.5%).  Measured default against default:
+// 2k-8k contexts and four sequences at 4k 1.6-5% faster, 1k and 16k-64k,
+// 32/4 and 16/2 heads at 32k and the Pareto batch within +-0.8%.
 constexpr double kWorkersPerSqrtChunk = 7.0;
+constexpr double kWorkersPerSqrtChunkMfma = 10.0;
+constexpr int64_t kMaxPiecesPerSegmentMfma = 160;
 // The vector kernel's segments are single query heads, so its pieces are a
 // head's row, and many heads per sequence give many short segments.  Below
 // kVectorSmallBatch chunks of T it takes 3 workers per CU (not 21 per 8 CUs)
@@ -199,7 +207,10 @@ int default_workers_for_call(int dtype, int head_dim, int block_size, int max_bl
   const int64_t segments = (int64_t)num_seqs * (mfma ? num_kv_heads : num_q_heads);
   const int64_t chunks = (int64_t)max_blocks_per_seq * block_size / 16;
   const double t = (double)segments * (double)(chunks > 0 ? chunks : 1);
-  int64_t cap = (int64_t)(kWorkersPerSqrtChunk * std::sqrt(t));
+  const double per_sqrt = mfma ? kWorkersPerSqrtChunkMfma : kWorkersPerSqrtChunk;
+  int64_t cap = (int64_t)(per_sqrt * std::sqrt(t));
+  const int64_t most = kMaxPiecesPerSegmentMfma * segments;
+  if (mfma && cap > most) cap = most;
   if (!mfma && t < kVectorSmallBatch) {
     workers = small > workers ? small : workers;
     const int64_t floor = kVectorPiecesPerSegment * segments;
@@ -692,8 +703,9 @@ constexpr int kPrefillSplitWgsPerCu = 2;        // target of the many-split choi
 // workgroups per compute unit (at most 32): on one 64/8-head sequence's
 // 64-token chunk over 32k, 16 splits (512 workgroups) took 89.4 us against
 // 92.3 at 24 (a full round), and on 40 heads' 64-token chunk over 32k, 12
-// (480) took 134.7 us against 161.8-186.2 at 20-32.  Otherwise S in [2, Smax], Smax = floor(2 slots / tiles) (at
-// least 2, at most 16), with the smallest per-CU share ceil(tiles S / CUs) / S
+// (480) took 134.7 us against 161.8-186.2 at 20-32.  Otherwise S in
+// [2, Smax], Smax = floor(2 slots / tiles) (at least 2, at most 16), with the
+// smallest per-CU share ceil(tiles S / CUs) / S
 // of one tile's work -- splits that leave some CUs a workgroup more than
 // others lose -- and among equal shares the most splits (more resident
 // workgroups).  Either way at most one split per 8 key steps of the longest
