@@ -12,7 +12,9 @@ pa_decode_shared for all 128 beams, each request's beams one group
 (``--plain``: pa_decode).
 
 Reported per step: wall-clock time of the whole step (host manager + uploads
-+ device work), the manager's share, device time of the copy and of the
++ device work), the host's shares (the manager with the survivor choice, the
+uploads -- synchronous copies from pageable memory, which wait for the step
+before -- and the launches), device time of the copy and of the
 decode (HIP events on the stream the calls use, sampled every 10th step so the
 events do not slow the loop), copies per step, and the decode's KV read rate
 in algorithmic bytes (every cached token's K and V rows of every beam, shared
@@ -81,7 +83,8 @@ def main():
     max_blocks = -(-(a.prompt + steps_total) // bs)
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    rec = {"wall": [], "mgr": [], "copy": [], "decode": [], "copies": [], "kv": []}
+    rec = {"wall": [], "mgr": [], "upload": [], "launch": [], "copy": [], "decode": [],
+           "copies": [], "kv": []}
 
     def step(sample: bool, timed: bool):
         nonlocal next_id
@@ -111,6 +114,8 @@ def main():
         tables_d = torch.from_numpy(tables).to(dev)
         lens_d = torch.from_numpy(lens).to(dev)
         copies_d = torch.from_numpy(copies).to(dev) if len(copies) else None
+        prefix_d = torch.from_numpy(prefix).to(dev) if a.shared else None
+        t2 = time.perf_counter()
         if sample:
             ev[0].record()
         if copies_d is not None:
@@ -119,7 +124,7 @@ def main():
             ev[1].record()
         if a.shared:
             pa.pa_decode_shared(q, k, v, tables_d, lens_d, float(scale), starts_d,
-                                torch.from_numpy(prefix).to(dev), out=out, k_new=kn, v_new=vn,
+                                prefix_d, out=out, k_new=kn, v_new=vn,
                                 slot_mapping=slots_d, workspace=ws)
         else:
             pa.pa_decode(q, k, v, tables_d, lens_d, float(scale), out=out, k_new=kn, v_new=vn,
@@ -131,7 +136,10 @@ def main():
             rec["decode"].append(ev[1].elapsed_time(ev[2]) * 1e3)
             rec["kv"].append(int(lens.astype(np.int64).sum()) * 2 * hkv * d * 2)
         if timed:
+            t3 = time.perf_counter()
             rec["mgr"].append((t1 - t0) * 1e6)
+            rec["upload"].append((t2 - t1) * 1e6)
+            rec["launch"].append((t3 - t2) * 1e6)
             rec["copies"].append(len(copies))
 
     for _ in range(a.warmup):
@@ -154,6 +162,8 @@ def main():
         "steps": a.steps, "pool_blocks": nb,
         "step_us_wall": round(wall, 1),
         "manager_us": round(float(np.median(rec["mgr"])), 1),
+        "upload_us": round(float(np.median(rec["upload"])), 1),
+        "launch_us": round(float(np.median(rec["launch"])), 1),
         "copy_gpu_us": round(float(np.median(rec["copy"])), 1),
         "decode_gpu_us": round(decode_us, 1),
         "copies_per_step": round(float(np.mean(rec["copies"])), 1),
