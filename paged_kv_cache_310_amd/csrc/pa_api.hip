@@ -166,7 +166,8 @@ int default_workers_for_variant(int dtype, int head_dim, int block_size, int gro
 }
 
 // Default workers of one call: the variant's count, or fewer for small
-// batches: about 7 sqrt(T) workers for T = segments x 16-token chunks of the
+// batches: about c sqrt(T) workers (c = 7 on the vector kernel, 10 on the
+// matrix-core kernel; the history below) for T = segments x 16-token chunks of the
 // table width (a segment is a (sequence, head) pair of the attention
 // kernel's line; the table width is the host's only bound on the contexts).
 // A segment split over more workers gains kernel time but costs the merge
@@ -213,8 +214,8 @@ int default_workers_for_call(int dtype, int head_dim, int block_size, int max_bl
   if (mfma && cap > most) cap = most;
   if (!mfma && t < kVectorSmallBatch) {
     workers = small > workers ? small : workers;
-    const int64_t floor = kVectorPiecesPerSegment * segments;
-    cap = floor > cap ? floor : cap;
+    const int64_t least = kVectorPiecesPerSegment * segments;
+    cap = least > cap ? least : cap;
   }
   cap = (cap + pa::kNumXcd - 1) / pa::kNumXcd * pa::kNumXcd;
   if (cap < pa::kNumXcd) cap = pa::kNumXcd;
