@@ -249,6 +249,8 @@ def _decode_need(size_fn, device_index: int, b: int, hq: int, hkv: int, d: int,
     if need is None:
         with torch.cuda.device(device_index):
             need = size_fn(b, hq, hkv, d, num_workers)
+        if len(_workspace_sizes) >= 4096:   # batch sizes vary from step to step: stay bounded
+            _workspace_sizes.clear()
         _workspace_sizes[key] = need
     return need
 
